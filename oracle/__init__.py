@@ -1,0 +1,20 @@
+"""CPU oracle for the Mamba-2 SSD chunked forward.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg may import this package; the product path (the HIP library and
+its Python binding) never does, and shares no code with it.
+
+Contents
+  recurrence : ``ssd_recurrence`` -- the token-by-token recurrence in plain C
+               (fp64), the definition every other result is checked against.
+  forms      : two independent restatements used to pin the recurrence --
+               the quadratic semiseparable-matrix form and the four-stage
+               chunked form -- plus the A = 0 closed form.
+
+Parity status: every function here is pinned by ``tests/test_oracle.py``
+(hand-derived golden values, closed forms, cross-form equality and
+invariants); none is "parity unpinned".
+"""
+from .recurrence import ssd_recurrence, build_oracle, oracle_max_threads  # noqa: F401
+from .forms import (ssd_quadratic, ssd_chunked, ssd_linear_attention_closed_form,  # noqa: F401
+                    discretize)
