@@ -1,0 +1,244 @@
+"""SSD chunked forward benchmark on one MI355X.
+
+A step is one full SSD forward (all kernels of the path) over one batch of
+synthetic inputs already resident in HBM.  Inputs and outputs rotate over
+several buffer sets whose total exceeds the 256 MB Infinity Cache, so each
+step reads its inputs from HBM rather than from a cache warmed by the
+previous step.
+
+Prints ONE JSON line: whole-step throughput (tokens/s), plus
+  roofline     -- the main-pass kernel (ssd_chunk_scan_kernel), timed live
+                  with HIP events recorded around its launch in every timed
+                  step; achieved = algorithmic bytes / its mean duration;
+  cpu_baseline -- the fp64 oracle on this host's cores over a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+from workloads import WORKLOADS, Workload, make_inputs
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "SSD fwd ms & tokens/s at [B,L,H,P,N,chunk,G]; % of MFMA/HBM roofline"
+# Published figure for [4,2048,16,64,128,128,4]: 0.632 ms on Ascend 910B3
+# (page "Mamba-2 SSD for Ascend NPU", Benchmark table) = 4*2048/0.632e-3 tokens/s.
+PAGE_TOKENS_PER_S = {"same_device": 4 * 2048 / 0.632e-3,
+                     "h256": 8 * 4096 / 31.888e-3}
+
+
+def algorithmic_bytes(w: Workload, ret_final: bool = True) -> int:
+    """Bytes the forward must move at least once: every input read once,
+    every output written once."""
+    s_io = 2 if w.io_dtype == "bf16" else 4
+    T, H, P, N, G = w.tokens, w.nheads, w.headdim, w.dstate, w.ngroups
+    b = T * H * P * s_io                     # x
+    b += T * H * P * 4                       # out (fp32)
+    b += (T * H * P * 4) if w.has_z else 0   # z (fp32)
+    b += 2 * T * G * N * s_io                # B, C
+    b += 4 * T * H                           # dt
+    b += 4 * H * (1 + (1 if w.has_D else 0))  # A, D
+    b += 4 * w.batch * H * P * N * ((1 if ret_final else 0) + (1 if w.has_h0 else 0))
+    return b
+
+
+def algorithmic_flops(w: Workload) -> int:
+    """Dense-tile MFMA flops of the chunked form: C.B^T, M.X, C.S^T, X^T.B."""
+    nc = -(-w.seqlen // w.chunk)
+    Q, N, P, G, H = w.chunk, w.dstate, w.headdim, w.ngroups, w.nheads
+    return 2 * w.batch * nc * (G * Q * Q * N + H * Q * Q * P + 2 * H * Q * N * P)
+
+
+class HipEvents:
+    """Raw HIP events via the HIP runtime (recorded inside the library)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> ctypes.c_void_p:
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return ev
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def gpu_input_set(w: Workload, seed: int, device: str):
+    """One more input set drawn directly on the GPU (same distributions)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    f32 = torch.float32
+    io = torch.bfloat16 if w.io_dtype == "bf16" else f32
+    Bsz, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    d = {"x": torch.randn(Bsz, L, H, P, generator=g, device=device, dtype=f32).to(io),
+         "dt": torch.rand(Bsz, L, H, generator=g, device=device, dtype=f32),
+         "A": -torch.rand(H, generator=g, device=device, dtype=f32),
+         "B": torch.randn(Bsz, L, G, N, generator=g, device=device, dtype=f32).to(io),
+         "C": torch.randn(Bsz, L, G, N, generator=g, device=device, dtype=f32).to(io)}
+    d["D"] = torch.randn(H, generator=g, device=device, dtype=f32) if w.has_D else None
+    d["z"] = torch.randn(Bsz, L, H, P, generator=g, device=device, dtype=f32) if w.has_z else None
+    d["initial_states"] = (0.1 * torch.randn(Bsz, H, P, N, generator=g, device=device, dtype=f32)
+                           if w.has_h0 else None)
+    return d
+
+
+def cpu_baseline(w: Workload, budget_s: float):
+    """The fp64 oracle, as it stands, on this host's cores, over a bounded
+    sample of (b, h) sequences of the same workload, scaled to tokens/s of
+    the whole workload."""
+    from oracle import oracle_max_threads, ssd_recurrence
+    d = make_inputs(w)
+    BH = w.batch * w.nheads
+    all_pairs = [(b, h) for b in range(w.batch) for h in range(w.nheads)]
+    threads = oracle_max_threads()
+    # probe with one pair per thread to size the sample
+    n = min(BH, max(1, threads))
+    t0 = time.perf_counter()
+    ssd_recurrence(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                   initial_states=d["initial_states"], dt_softplus=True, pairs=all_pairs[:n])
+    t_probe = time.perf_counter() - t0
+    per_pair = t_probe / n * threads if n >= threads else t_probe
+    n_pairs = int(min(BH, max(n, budget_s / max(per_pair, 1e-9) * threads)))
+    n_pairs = max(threads, (n_pairs // threads) * threads) if n_pairs >= threads else n_pairs
+    n_pairs = min(n_pairs, BH)
+    step = max(1, BH // n_pairs)
+    pairs = all_pairs[::step][:n_pairs]
+    t0 = time.perf_counter()
+    ssd_recurrence(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                   initial_states=d["initial_states"], dt_softplus=True, pairs=pairs)
+    t = time.perf_counter() - t0
+    frac = len(pairs) / BH
+    t_full = t / frac
+    return {"value": w.tokens / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(pairs)} of {BH} (b,h) sequences of the full {w.shape_str()} workload "
+                      f"({t:.1f} s, fp64, {threads} OpenMP threads); scaled to all {BH}"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="same_device", choices=sorted(WORKLOADS))
+    ap.add_argument("--mma", default="f16", choices=["f16", "f32"])
+    ap.add_argument("--chunks-per-wg", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = auto)")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+              f"multi-GPU path; see DESIGN.md for how the SSD forward would shard.", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    import mamba_ssd_chunked_04_amd as ssd
+    ssd.load_library()
+    w = WORKLOADS[args.config]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    print(f"[bench] workload {w.name} {w.shape_str()} mma={args.mma}", file=sys.stderr, flush=True)
+
+    # rotating input/output sets: total footprint > 2 x 256 MB Infinity Cache
+    abytes = algorithmic_bytes(w)
+    n_sets = args.sets or max(1, min(16, math.ceil(2 * 512e6 / abytes)))
+    sets = [{k: (None if v is None else v.to(dev)) for k, v in make_inputs(w).items()}]
+    for s in range(1, n_sets):
+        sets.append(gpu_input_set(w, w.seed * 1000 + s, dev))
+    ev = HipEvents()
+    calls = []
+    for d in sets:
+        call, out, fin, wsp = ssd.prepare(d["x"], d["dt"], d["A"], d["B"], d["C"], w.chunk,
+                                          D=d["D"], z=d["z"], initial_states=d["initial_states"],
+                                          dt_softplus=True, return_final_state=True, mma=args.mma,
+                                          chunks_per_wg=args.chunks_per_wg)
+        calls.append(call)
+    cpg, ngroups = ssd.plan(calls[0].desc, w.chunk)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    for k in range(args.warmup):
+        calls[k % n_sets].launch(stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(ev.create(), ev.create()) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        c = calls[k % n_sets]
+        c.desc.ev_main_begin, c.desc.ev_main_end = evs[k][0].value, evs[k][1].value
+        c.launch(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for c in calls:
+        c.desc.ev_main_begin = c.desc.ev_main_end = None
+    main_ms = [ev.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    ms_per_step = wall / K * 1e3
+    tok_s = w.tokens / (wall / K)
+    main_mean = sum(main_ms) / len(main_ms)
+    achieved = abytes / (main_mean * 1e-3) / 1e9
+    flops = algorithmic_flops(w)
+    rec = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (tok_s / PAGE_TOKENS_PER_S[w.name]) if w.name in PAGE_TOKENS_PER_S else None,
+        "dtype": "f16" if args.mma == "f16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} {w.shape_str()}", "B": w.batch, "L": w.seqlen,
+                   "H": w.nheads, "P": w.headdim, "N": w.dstate, "chunk": w.chunk,
+                   "G": w.ngroups, "io_dtype": w.io_dtype, "D": w.has_D, "z": w.has_z,
+                   "initial_state": w.has_h0, "final_state": True,
+                   "chunks_per_wg": cpg, "chunk_groups": ngroups, "input_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "ssd_chunk_scan_kernel", "kernel_ms": main_mean,
+                     "algorithmic_bytes": abytes},
+        "path": {"ms": ms_per_step, "gbs": abytes / (wall / K) / 1e9,
+                 "hbm_frac": abytes / (wall / K) / 1e9 / HBM_PEAK_GBS,
+                 "tflops": flops / (wall / K) / 1e12},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_baseline_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

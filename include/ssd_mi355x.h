@@ -1,0 +1,136 @@
+/*
+ * ssd_mi355x.h -- C ABI of the Mamba-2 SSD chunked forward for MI355X (gfx950).
+ *
+ * The operation (page "ops-transformer MambaV2 算子套件", §1.1 and §1.3; tensor
+ * semantics of page "Mamba-2 SSD for Ascend NPU", section "Implementation"):
+ * for each batch row b and head h, with group g = h / (H/G),
+ *
+ *   delta_t = clamp(softplus(dt[b,t,h] + dt_bias[h]), dt_min, dt_max)
+ *   S_t     = exp(delta_t A[h]) S_{t-1} + delta_t x[b,t,h,:] (outer) B[b,t,g,:]
+ *   out[b,t,h,:] = (S_t . C[b,t,g,:] + D[h] x[b,t,h,:]) * silu(z[b,t,h,:])
+ *   final_state[b,h] = S_{L-1}
+ *
+ * computed chunk by chunk the way that page's §2 and §4.2-§4.5 chain it:
+ * in-chunk cumulative decay (chunk_cumsum), per-chunk states (chunk_state),
+ * the sequential inter-chunk recurrence (chunk_state_passing), and the
+ * intra-chunk masked C.B^T product plus the inter-chunk term (chunk_scan).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, dense and
+ *     row-major with the shapes given below, 16-byte aligned.  The library
+ *     never allocates, frees or keeps them after a call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream) and the call returns without synchronising.
+ *     Device faults therefore surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid or unsupported call returns an error and launches nothing.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  No exception or abort ever crosses this ABI. */
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = 1,  /* NULL required pointer, dim < 1, H % G != 0,
+                               misaligned pointer, bad dtype/mma code,
+                               final_state NULL while requested       */
+  SSD_ERR_UNSUPPORTED = 2,  /* valid but not compiled: headdim != 64,
+                               dstate not in {64,128}, chunk not in
+                               {64,128,256}                           */
+  SSD_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than required */
+  SSD_ERR_LAUNCH = 4        /* the HIP runtime rejected a launch       */
+} ssd_status;
+
+/* Storage dtypes. */
+typedef enum { SSD_F32 = 0, SSD_F16 = 1, SSD_BF16 = 2 } ssd_dtype;
+
+/* Matrix-core operand precision.  SSD_MMA_F16: x, B, C, the masked C.B^T
+ * weights, the decay-weighted B and the carried state are rounded to fp16
+ * for the MFMA products, accumulating in fp32 (the mixed precision the page
+ * "Mamba-2 SSD for Ascend NPU" describes for its Cube units).  SSD_MMA_F32:
+ * every operand stays fp32 (a slower check path). */
+typedef enum { SSD_MMA_F16 = 0, SSD_MMA_F32 = 2 } ssd_mma;
+
+/* Shape, dtypes and optional inputs of one call. */
+typedef struct ssd_desc {
+  int64_t batch;     /* B  >= 1 */
+  int64_t seqlen;    /* L  >= 1 (any length; a ragged last chunk is masked) */
+  int64_t nheads;    /* H  >= 1 */
+  int64_t headdim;   /* P  == 64 */
+  int64_t dstate;    /* N  in {64, 128} */
+  int64_t ngroups;   /* G  >= 1, H % G == 0; head h reads B/C group h/(H/G) */
+  int32_t x_dtype;   /* dtype of x, B and C: SSD_F32 or SSD_BF16 */
+  int32_t z_dtype;   /* dtype of z: SSD_F32 or SSD_BF16 (ignored when z NULL) */
+  int32_t out_dtype; /* dtype of out: SSD_F32 or SSD_BF16 */
+  int32_t mma;       /* ssd_mma */
+  float dt_min;      /* dt_limit lower bound (0 for none) */
+  float dt_max;      /* dt_limit upper bound (+INFINITY for none) */
+  const void *z;             /* [B,L,H,P] gate, or NULL (no gate)            */
+  const float *dt_bias;      /* [H] fp32, or NULL (zero)                      */
+  const float *initial_state;/* [B,H,P,N] fp32, or NULL (zero state)          */
+  void *workspace;           /* device scratch owned by the caller            */
+  size_t workspace_bytes;    /* its size; see ssd_fwd_workspace_size          */
+  int32_t chunks_per_wg;     /* chunks one workgroup walks in sequence; 0 picks
+                                automatically (see ssd_fwd_plan)              */
+  int32_t reserved;          /* must be 0 */
+  void *ev_main_begin;       /* optional hipEvent_t (as void*) recorded on the
+                                stream right before the main-pass kernel, for
+                                measurement; NULL records nothing             */
+  void *ev_main_end;         /* optional hipEvent_t recorded right after it   */
+} ssd_desc;
+
+/* Fills `d` with defaults for the given shape: fp32 storage, fp16 MMA, no
+ * optional inputs, no dt_limit, automatic plan, no workspace. */
+void ssd_desc_init(ssd_desc *d, int64_t batch, int64_t seqlen, int64_t nheads,
+                   int64_t headdim, int64_t dstate, int64_t ngroups);
+
+/* Bytes of device workspace ssd_fwd needs for this descriptor and chunk size
+ * (0 when one workgroup walks the whole sequence).  Errors as ssd_fwd's
+ * validation of shapes and codes (pointers are not looked at). */
+ssd_status ssd_fwd_workspace_size(const ssd_desc *d, int64_t chunk,
+                                  size_t *bytes);
+
+/* The plan ssd_fwd will use: chunks walked by one workgroup and the number
+ * of such chunk groups per (b, h).  With more than one group, the states of
+ * all but the last group are summed in a first pass, chained across groups
+ * (page "ops-transformer MambaV2 算子套件", §4.4) and fed to the main pass. */
+ssd_status ssd_fwd_plan(const ssd_desc *d, int64_t chunk,
+                        int64_t *chunks_per_wg, int64_t *n_chunk_groups);
+
+/* SSD chunked forward.
+ *   x      [B,L,H,P]  x_dtype          dt  [B,L,H]  fp32 (raw step)
+ *   A      [H]        fp32             B,C [B,L,G,N] x_dtype
+ *   D      [H]        fp32 or NULL     chunk: 64, 128 or 256 tokens
+ *   dt_softplus: nonzero applies softplus to dt + dt_bias before the clamp
+ *   return_final_state: nonzero writes final_state [B,H,P,N] fp32
+ *   out    [B,L,H,P]  out_dtype, fully overwritten (never accumulated)
+ * The tensor semantics follow page "Mamba-2 SSD for Ascend NPU", section
+ * "Implementation" (x, dt, A, B, C, initial_states, out, final_state; D, z,
+ * dt_bias, dt_softplus, dt_limit, return_final_state). */
+ssd_status ssd_fwd(const void *x, const float *dt, const float *A,
+                   const void *B, const void *C, const float *D,
+                   int64_t chunk, int dt_softplus, int return_final_state,
+                   void *out, float *final_state, void *stream,
+                   const ssd_desc *d);
+
+/* Static, human-readable name of a status code. */
+const char *ssd_status_str(int status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int ssd_abi_version(void);
+
+#define SSD_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_MI355X_H */

@@ -1,0 +1,11 @@
+"""Mamba-2 SSD chunked forward on MI355X (gfx950).
+
+The compute path is the HIP library libssd_mi355x.so (C ABI in
+include/ssd_mi355x.h); this package only binds it.  PyTorch supplies device
+memory and streams.
+"""
+from .binding import (EXPORTED_SYMBOLS, SsdCall, SsdDesc, SsdError, load_library,  # noqa: F401
+                      make_desc, plan, prepare, ssd_fwd, status_str, workspace_size)
+
+__all__ = ["ssd_fwd", "prepare", "plan", "workspace_size", "load_library", "make_desc",
+           "SsdCall", "SsdDesc", "SsdError", "status_str", "EXPORTED_SYMBOLS"]

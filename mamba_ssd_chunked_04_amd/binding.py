@@ -1,0 +1,216 @@
+"""Python binding of libssd_mi355x.so (include/ssd_mi355x.h), via ctypes.
+
+Argument marshalling only: every step of the SSD forward runs in the HIP
+kernels behind ``ssd_fwd``.  PyTorch provides device memory and the stream.
+There is no CPU fallback: a missing library or a non-GPU tensor raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+from .build import LIB
+
+SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_LAUNCH = range(5)
+SSD_F32, SSD_F16, SSD_BF16 = 0, 1, 2
+SSD_MMA_F16, SSD_MMA_F32 = 0, 2
+
+# Every symbol include/ssd_mi355x.h declares.
+EXPORTED_SYMBOLS = ("ssd_desc_init", "ssd_fwd_workspace_size", "ssd_fwd_plan", "ssd_fwd",
+                    "ssd_status_str", "ssd_abi_version")
+
+
+class SsdDesc(ctypes.Structure):
+    """Mirror of ``ssd_desc``."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+        ("x_dtype", ctypes.c_int32), ("z_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("mma", ctypes.c_int32),
+        ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
+        ("z", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("chunks_per_wg", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p),
+    ]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (built in-tree by ``build.build_library``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or os.environ.get("SSD_MI355X_LIB", LIB)
+    if not os.path.exists(p):
+        raise RuntimeError(f"HIP library {p} is missing: run __graft_entry__.build() "
+                           f"(or python -m mamba_ssd_chunked_04_amd.build) first")
+    lib = ctypes.CDLL(p)
+    vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    dp = ctypes.POINTER(SsdDesc)
+    lib.ssd_desc_init.argtypes = [dp, i64, i64, i64, i64, i64, i64]
+    lib.ssd_desc_init.restype = None
+    lib.ssd_fwd_workspace_size.argtypes = [dp, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssd_fwd_workspace_size.restype = c_int
+    lib.ssd_fwd_plan.argtypes = [dp, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.ssd_fwd_plan.restype = c_int
+    lib.ssd_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, c_int, c_int, vp, vp, vp, dp]
+    lib.ssd_fwd.restype = c_int
+    lib.ssd_status_str.argtypes = [c_int]
+    lib.ssd_status_str.restype = ctypes.c_char_p
+    lib.ssd_abi_version.argtypes = []
+    lib.ssd_abi_version.restype = c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().ssd_status_str(int(status)).decode()
+
+
+def _raise_for(status: int, what: str):
+    if status == SSD_OK:
+        return
+    msg = f"{what}: {status_str(status)}"
+    if status == SSD_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    if status in (SSD_ERR_INVALID_ARG, SSD_ERR_WORKSPACE):
+        raise ValueError(msg)
+    raise SsdError(status, msg)
+
+
+def make_desc(batch, seqlen, nheads, headdim, dstate, ngroups) -> SsdDesc:
+    d = SsdDesc()
+    load_library().ssd_desc_init(ctypes.byref(d), batch, seqlen, nheads, headdim, dstate, ngroups)
+    return d
+
+
+def workspace_size(desc: SsdDesc, chunk: int) -> int:
+    n = ctypes.c_size_t(0)
+    _raise_for(load_library().ssd_fwd_workspace_size(ctypes.byref(desc), int(chunk), ctypes.byref(n)),
+               "ssd_fwd_workspace_size")
+    return int(n.value)
+
+
+def plan(desc: SsdDesc, chunk: int) -> Tuple[int, int]:
+    """(chunks walked per workgroup, chunk groups per (b, h))."""
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    _raise_for(load_library().ssd_fwd_plan(ctypes.byref(desc), int(chunk), ctypes.byref(a),
+                                           ctypes.byref(b)), "ssd_fwd_plan")
+    return int(a.value), int(b.value)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16, torch.float16: SSD_F16}[t]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class SsdCall:
+    """One prepared ``ssd_fwd`` call over fixed tensors (for repeated launches).
+
+    Built by ``prepare``; ``launch(stream)`` enqueues the kernels on the given
+    stream handle (an int from ``torch.cuda.Stream.cuda_stream``).
+    """
+
+    def __init__(self, args, desc: SsdDesc, keep):
+        self._args = args
+        self.desc = desc
+        self._keep = keep        # tensors whose storage the pointers refer to
+
+    def launch(self, stream: int) -> None:
+        a = self._args
+        st = load_library().ssd_fwd(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9],
+                                    a[10], ctypes.c_void_p(stream), ctypes.byref(self.desc))
+        _raise_for(st, "ssd_fwd")
+
+
+def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initial_states=None,
+            dt_softplus: bool = False, dt_limit: Tuple[float, float] = (0.0, math.inf),
+            return_final_state: bool = False, mma: str = "f16", out_dtype=None,
+            chunks_per_wg: int = 0, out=None, final_state=None, workspace=None):
+    """Validate torch tensors, allocate outputs/workspace, and build an SsdCall.
+
+    ``out`` is float32 unless ``out_dtype`` (float32 or bfloat16) says
+    otherwise, whatever the dtype of x, B and C.
+    Returns (call, out, final_state_or_None, workspace_or_None).
+    """
+    import torch
+    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    dev = x.device
+    Bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if dt.shape != (Bsz, L, H) or A.shape != (H,) or B.shape != (Bsz, L, G, N) or C.shape != B.shape:
+        raise ValueError("shape mismatch: x[B,L,H,P], dt[B,L,H], A[H], B/C[B,L,G,N]")
+    if B.dtype != x.dtype or C.dtype != x.dtype:
+        raise ValueError("x, B and C must share one dtype")
+    for name, t in (("dt", dt), ("A", A), ("D", D), ("dt_bias", dt_bias),
+                    ("initial_states", initial_states)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    opt_shapes = (("D", D, (H,)), ("dt_bias", dt_bias, (H,)), ("z", z, (Bsz, L, H, P)),
+                  ("initial_states", initial_states, (Bsz, H, P, N)))
+    for name, t, shp in opt_shapes:
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} must have shape {shp}")
+    tensors = [x, dt, A, B, C, D, z, dt_bias, initial_states]
+    for t in tensors:
+        if t is not None and (t.device != dev or not t.is_contiguous()):
+            raise ValueError("all tensors must be contiguous and on the same GPU")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(Bsz, L, H, P, device=dev, dtype=out_dtype)
+    if return_final_state and final_state is None:
+        final_state = torch.empty(Bsz, H, P, N, device=dev, dtype=torch.float32)
+    desc = make_desc(Bsz, L, H, P, N, G)
+    desc.x_dtype = _dtype_code(x.dtype)
+    desc.z_dtype = _dtype_code(z.dtype) if z is not None else SSD_F32
+    desc.out_dtype = _dtype_code(out.dtype)
+    desc.mma = {"f16": SSD_MMA_F16, "f32": SSD_MMA_F32}[mma]
+    desc.dt_min, desc.dt_max = float(dt_limit[0]), float(dt_limit[1])
+    desc.z, desc.dt_bias, desc.initial_state = _ptr(z), _ptr(dt_bias), _ptr(initial_states)
+    desc.chunks_per_wg = int(chunks_per_wg)
+    nbytes = workspace_size(desc, chunk_size)
+    if nbytes > 0 and workspace is None:
+        workspace = torch.empty(nbytes, device=dev, dtype=torch.uint8)
+    if workspace is not None:
+        desc.workspace, desc.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk_size),
+            int(bool(dt_softplus)), int(bool(return_final_state)), _ptr(out),
+            _ptr(final_state) if return_final_state else None)
+    keep = (x, dt, A, B, C, D, z, dt_bias, initial_states, out, final_state, workspace)
+    return SsdCall(args, desc, keep), out, (final_state if return_final_state else None), workspace
+
+
+def ssd_fwd(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initial_states=None,
+            dt_softplus: bool = False, dt_limit: Tuple[float, float] = (0.0, math.inf),
+            return_final_state: bool = False, mma: str = "f16", out_dtype=None,
+            chunks_per_wg: int = 0):
+    """SSD chunked forward on the current torch stream.
+
+    Returns ``out`` or ``(out, final_state)`` when ``return_final_state``.
+    """
+    import torch
+    call, out, fin, _ws = prepare(x, dt, A, B, C, chunk_size, D=D, z=z, dt_bias=dt_bias,
+                                  initial_states=initial_states, dt_softplus=dt_softplus,
+                                  dt_limit=dt_limit, return_final_state=return_final_state,
+                                  mma=mma, out_dtype=out_dtype, chunks_per_wg=chunks_per_wg)
+    with torch.cuda.device(x.device):
+        call.launch(torch.cuda.current_stream(x.device).cuda_stream)
+    return (out, fin) if return_final_state else out

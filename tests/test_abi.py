@@ -1,0 +1,177 @@
+"""Host-side checks of the C-ABI library (no GPU needed, nothing is launched).
+
+* the library loads and exports every function include/*.h declares;
+* the ctypes mirror of ssd_desc matches the C layout (via ssd_desc_init);
+* every validation error path returns its status code before any launch
+  (fake, never-dereferenced device pointers are used, so each call below has
+  at least one invalid argument);
+* workspace sizes and plans for the five workloads.
+"""
+import ctypes
+import glob
+import math
+import os
+import re
+
+import pytest
+
+import mamba_ssd_chunked_04_amd as ssd
+from mamba_ssd_chunked_04_amd import binding as bnd
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(path).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        for m in re.finditer(r"\b(ssd_[a-z0-9_]+)\s*\(", src):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ssd.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert declared, "no declarations found"
+    assert declared == set(bnd.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+    assert lib.ssd_abi_version() == 1
+
+
+def test_desc_layout_matches_c(lib):
+    assert ctypes.sizeof(bnd.SsdDesc) == 136
+    d = bnd.SsdDesc()
+    ctypes.memset(ctypes.byref(d), 0x5A, ctypes.sizeof(d))
+    lib.ssd_desc_init(ctypes.byref(d), 3, 5, 7, 64, 128, 7)
+    assert (d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.ngroups) == (3, 5, 7, 64, 128, 7)
+    assert (d.x_dtype, d.z_dtype, d.out_dtype, d.mma) == (bnd.SSD_F32, bnd.SSD_F32, bnd.SSD_F32,
+                                                          bnd.SSD_MMA_F16)
+    assert d.dt_min == 0.0 and math.isinf(d.dt_max)
+    assert d.z is None and d.dt_bias is None and d.initial_state is None and d.workspace is None
+    assert d.workspace_bytes == 0 and d.chunks_per_wg == 0 and d.reserved == 0
+    assert d.ev_main_begin is None and d.ev_main_end is None
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = ssd.status_str(code)
+        assert s.startswith("SSD_")
+    assert "unknown" in ssd.status_str(99)
+
+
+FAKE = 0x10000   # 16-byte aligned, never dereferenced
+
+
+def _call(lib, desc, chunk=64, x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, ret_final=0,
+          out=FAKE, fin=None):
+    return lib.ssd_fwd(x, dt, A, B, C, D, chunk, 1, ret_final, out, fin, None,
+                       ctypes.byref(desc) if desc is not None else None)
+
+
+def _desc(**kw):
+    d = bnd.make_desc(kw.pop("B", 1), kw.pop("L", 128), kw.pop("H", 4), kw.pop("P", 64),
+                      kw.pop("N", 64), kw.pop("G", 2))
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("field,value", [("batch", 0), ("seqlen", 0), ("nheads", 0),
+                                         ("headdim", 0), ("dstate", -1), ("ngroups", 0),
+                                         ("ngroups", 3), ("x_dtype", 9), ("z_dtype", -1),
+                                         ("out_dtype", 7), ("mma", 1), ("chunks_per_wg", -2),
+                                         ("reserved", 1)])
+def test_invalid_descriptor_fields(lib, field, value):
+    d = _desc()
+    setattr(d, field, value)
+    assert _call(lib, d) == bnd.SSD_ERR_INVALID_ARG
+
+
+def test_invalid_dt_limit(lib):
+    d = _desc(dt_min=2.0, dt_max=1.0)
+    assert _call(lib, d) == bnd.SSD_ERR_INVALID_ARG
+    d = _desc(dt_min=float("nan"))
+    assert _call(lib, d) == bnd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("arg", ["x", "dt", "A", "B", "C", "out"])
+def test_null_required_pointer(lib, arg):
+    d = _desc()
+    assert _call(lib, d, **{arg: None}) == bnd.SSD_ERR_INVALID_ARG
+
+
+def test_null_descriptor(lib):
+    assert _call(lib, None) == bnd.SSD_ERR_INVALID_ARG
+
+
+def test_final_state_requested_but_null(lib):
+    assert _call(lib, _desc(), ret_final=1, fin=None) == bnd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("arg", ["x", "B", "C", "out", "dt"])
+def test_misaligned_pointer(lib, arg):
+    assert _call(lib, _desc(), **{arg: FAKE + 4}) == bnd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,chunk", [({"P": 32}, 64), ({"P": 128}, 64), ({"N": 32}, 64),
+                                      ({"N": 256}, 64), ({}, 32), ({}, 512), ({}, 100),
+                                      ({"x_dtype": bnd.SSD_F16}, 64),
+                                      ({"out_dtype": bnd.SSD_F16}, 64)])
+def test_unsupported(lib, kw, chunk):
+    assert _call(lib, _desc(**kw), chunk=chunk) == bnd.SSD_ERR_UNSUPPORTED
+
+
+def test_workspace_missing_or_small(lib):
+    # 1 x 4096 tokens, 2 heads: the automatic plan splits the sequence, so a
+    # workspace is needed
+    d = _desc(L=4096, H=2, G=1)
+    need = ssd.workspace_size(d, 64)
+    assert need > 0
+    assert _call(lib, d) == bnd.SSD_ERR_WORKSPACE
+    d.workspace, d.workspace_bytes = FAKE, need - 1
+    assert _call(lib, d) == bnd.SSD_ERR_WORKSPACE
+    d.workspace, d.workspace_bytes = FAKE + 8, need
+    assert _call(lib, d) == bnd.SSD_ERR_WORKSPACE
+
+
+def test_workspace_size_errors(lib):
+    n = ctypes.c_size_t(0)
+    d = _desc()
+    assert lib.ssd_fwd_workspace_size(ctypes.byref(d), 64, None) == bnd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_fwd_workspace_size(None, 64, ctypes.byref(n)) == bnd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_fwd_workspace_size(ctypes.byref(d), 48, ctypes.byref(n)) == bnd.SSD_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_plans(lib, name):
+    w = WORKLOADS[name]
+    d = bnd.make_desc(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups)
+    cpg, ng = ssd.plan(d, w.chunk)
+    nc = -(-w.seqlen // w.chunk)
+    assert 1 <= cpg <= nc and ng == -(-nc // cpg)
+    ws = ssd.workspace_size(d, w.chunk)
+    slots = w.batch * w.nheads * (ng - 1)
+    assert ws >= slots * (w.headdim * w.dstate + 1) * 4
+    if ng == 1:
+        assert ws == 0
+    # explicit override
+    d.chunks_per_wg = 1
+    assert ssd.plan(d, w.chunk) == (1, nc)
+
+
+def test_product_path_does_not_touch_oracle():
+    """The HIP path and its binding never import or load the oracle."""
+    pkg = os.path.join(ROOT, "mamba_ssd_chunked_04_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if os.path.isfile(path) and path.endswith((".py", ".hip", ".h", ".cpp")):
+            src = open(path, encoding="utf-8").read()
+            assert "oracle" not in src.lower(), path

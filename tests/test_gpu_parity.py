@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Bar (per output tensor): max|gpu - oracle| <= tol * max|oracle|, with
+tol = 2e-3 on the fp16-operand MFMA path and 1e-4 on the all-fp32 check
+path; the same bound applies to final_state against max|final_state|.
+NRMSE and cosine similarity are printed alongside.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ssd_recurrence
+from workloads import WORKLOADS, make_inputs, random_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f16": 2e-3, "f32": 1e-4}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def metrics(got: np.ndarray, ref: np.ndarray):
+    diff = np.abs(got - ref)
+    scale = float(np.abs(ref).max())
+    rel = float(diff.max()) / scale if scale > 0 else float(diff.max())
+    nrmse = float(np.sqrt(np.mean((got - ref) ** 2)) / (np.sqrt(np.mean(ref ** 2)) + 1e-300))
+    cos = float(np.sum(got * ref) / (np.linalg.norm(got) * np.linalg.norm(ref) + 1e-300))
+    return rel, nrmse, cos
+
+
+def assert_close(got, ref, tol, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    rel, nrmse, cos = metrics(got, ref)
+    _say(f"    {what}: max_err/max_ref={rel:.3e} nrmse={nrmse:.3e} cos={cos:.9f} (tol {tol:g})")
+    assert rel <= tol, f"{what}: max_err/max_ref={rel:.3e} > {tol:g}"
+
+
+def to_gpu(d):
+    return {k: (None if v is None else v.cuda()) for k, v in d.items()}
+
+
+def gpu_run(ssd, d, chunk, mma="f16", softplus=True, limit=(0.0, math.inf), chunks_per_wg=0,
+            ret_final=True, out_dtype=None):
+    g = to_gpu(d)
+    res = ssd.ssd_fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], chunk, D=g.get("D"), z=g.get("z"),
+                      dt_bias=g.get("dt_bias"), initial_states=g.get("initial_states"),
+                      dt_softplus=softplus, dt_limit=limit, return_final_state=ret_final, mma=mma,
+                      out_dtype=out_dtype, chunks_per_wg=chunks_per_wg)
+    torch.cuda.synchronize()
+    if ret_final:
+        out, fin = res
+        return out.float().cpu().numpy(), fin.cpu().numpy()
+    return res.float().cpu().numpy(), None
+
+
+def oracle_run(d, softplus=True, limit=(0.0, math.inf)):
+    return ssd_recurrence(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d.get("D"), z=d.get("z"),
+                          dt_bias=d.get("dt_bias"), initial_states=d.get("initial_states"),
+                          dt_softplus=softplus, dt_limit=limit)
+
+
+# (name, B, L, H, N, G, chunk, D, z, h0, dt_bias, io, limit)
+SMALL = [
+    ("q64_tail", 2, 300, 4, 64, 2, 64, False, False, False, False, "f32", None),
+    ("q128_tail_D_h0", 1, 700, 3, 128, 1, 128, True, False, True, False, "f32", None),
+    ("q256_tail_all", 2, 600, 8, 128, 2, 256, True, True, True, True, "f32", None),
+    ("q64_n128_bf16", 1, 257, 4, 128, 4, 64, True, True, True, False, "bf16", None),
+    ("q128_n64_limit", 2, 390, 2, 64, 1, 128, False, False, False, True, "f32", (0.8, 1.1)),
+    ("q256_n64_bf16_gate", 1, 513, 4, 64, 2, 256, True, True, False, False, "bf16", None),
+]
+
+
+@pytest.mark.parametrize("mma", ["f16", "f32"])
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes(gpu_lib, case, mma):
+    name, Bsz, L, H, N, G, Q, hD, hz, hh, hb, io, limit = case
+    limit = limit or (0.0, math.inf)
+    _say(f"[case] {name} mma={mma} shape=[{Bsz},{L},{H},64,{N},{Q},{G}]")
+    d = random_inputs(Bsz, L, H, 64, N, G, seed=100 + len(name), has_D=hD, has_z=hz, has_h0=hh,
+                      io_dtype=io, dt_bias=hb)
+    ref_out, ref_fin = oracle_run(d, limit=limit)
+    for cpw in (0, 1, 2):
+        out, fin = gpu_run(gpu_lib, d, Q, mma=mma, limit=limit, chunks_per_wg=cpw)
+        assert_close(out, ref_out, TOL[mma], f"out (chunks_per_wg={cpw})")
+        assert_close(fin, ref_fin, TOL[mma], f"final_state (chunks_per_wg={cpw})")
+
+
+@pytest.mark.parametrize("mma", ["f16", "f32"])
+def test_tiny_workload(gpu_lib, mma):
+    w = WORKLOADS["tiny"]
+    _say(f"[case] tiny workload {w.shape_str()} mma={mma}")
+    d = make_inputs(w)
+    ref_out, ref_fin = oracle_run(d)
+    out, fin = gpu_run(gpu_lib, d, w.chunk, mma=mma)
+    assert_close(out, ref_out, TOL[mma], "out")
+    assert_close(fin, ref_fin, TOL[mma], "final_state")
+
+
+@pytest.mark.parametrize("L", [1, 5, 16, 63, 65, 129])
+def test_short_and_ragged_sequences(gpu_lib, L):
+    _say(f"[case] short L={L}")
+    d = random_inputs(2, L, 4, 64, 64, 2, seed=300 + L, has_D=True, has_h0=True)
+    ref_out, ref_fin = oracle_run(d)
+    for Q in (64, 128, 256):
+        out, fin = gpu_run(gpu_lib, d, Q)
+        assert_close(out, ref_out, TOL["f16"], f"out Q={Q}")
+        assert_close(fin, ref_fin, TOL["f16"], f"final Q={Q}")
+
+
+def test_no_final_state_and_bf16_out(gpu_lib):
+    d = random_inputs(1, 200, 2, 64, 128, 1, seed=401, has_z=True)
+    ref_out, _ = oracle_run(d)
+    out, fin = gpu_run(gpu_lib, d, 128, ret_final=False, out_dtype=torch.bfloat16)
+    assert fin is None
+    # bf16 storage adds up to 2^-9 relative rounding per element
+    assert_close(out, ref_out, TOL["f16"] + 2 ** -8, "out (bf16 storage)")
+
+
+def test_determinism(gpu_lib):
+    d = random_inputs(2, 700, 8, 64, 128, 2, seed=402, has_D=True, has_z=True, has_h0=True)
+    a_out, a_fin = gpu_run(gpu_lib, d, 256, chunks_per_wg=1)
+    b_out, b_fin = gpu_run(gpu_lib, d, 256, chunks_per_wg=1)
+    np.testing.assert_array_equal(a_out, b_out)
+    np.testing.assert_array_equal(a_fin, b_fin)
+
+
+def test_guard_bands_untouched(gpu_lib):
+    d = random_inputs(1, 333, 4, 64, 128, 2, seed=403, has_h0=True)
+    g = to_gpu(d)
+    n_out = 1 * 333 * 4 * 64
+    n_fin = 1 * 4 * 64 * 128
+    pad = 1024
+    big = torch.full((n_out + 2 * pad,), float("nan"), device="cuda")
+    bigf = torch.full((n_fin + 2 * pad,), float("nan"), device="cuda")
+    out = big[pad:pad + n_out].view(1, 333, 4, 64)
+    fin = bigf[pad:pad + n_fin].view(1, 4, 64, 128)
+    call, _, _, _ = gpu_lib.prepare(g["x"], g["dt"], g["A"], g["B"], g["C"], 128,
+                                    initial_states=g["initial_states"], dt_softplus=True,
+                                    return_final_state=True, out=out, final_state=fin)
+    call.launch(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.isnan(big[:pad]).all() and torch.isnan(big[pad + n_out:]).all()
+    assert torch.isnan(bigf[:pad]).all() and torch.isnan(bigf[pad + n_fin:]).all()
+    ref_out, ref_fin = oracle_run(d)
+    assert_close(out.cpu().numpy(), ref_out, TOL["f16"], "out")
+    assert_close(fin.cpu().numpy(), ref_fin, TOL["f16"], "final_state")
+
+
+def test_invalid_calls_raise(gpu_lib):
+    d = to_gpu(random_inputs(1, 64, 2, 64, 64, 1, seed=404))
+    with pytest.raises(NotImplementedError):
+        gpu_lib.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], 32)
+    with pytest.raises(ValueError):
+        gpu_lib.ssd_fwd(d["x"].cpu(), d["dt"], d["A"], d["B"], d["C"], 64)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _pair_slice(d, b, h, H, G):
+    g = h // (H // G)
+    s = {"x": d["x"][b:b + 1, :, h:h + 1], "dt": d["dt"][b:b + 1, :, h:h + 1],
+         "A": d["A"][h:h + 1], "B": d["B"][b:b + 1, :, g:g + 1], "C": d["C"][b:b + 1, :, g:g + 1]}
+    s["D"] = None if d["D"] is None else d["D"][h:h + 1]
+    s["z"] = None if d["z"] is None else d["z"][b:b + 1, :, h:h + 1]
+    s["initial_states"] = None if d["initial_states"] is None else d["initial_states"][b:b + 1, h:h + 1]
+    return s
+
+
+@pytest.mark.parametrize("name", ["same_device", "h256", "long", "gated"])
+def test_full_workload_sampled_pairs(gpu_lib, name):
+    """Full-size workload in the launch configuration the benchmark times;
+    the oracle recomputes a sample of (b, h) sequences end to end."""
+    w = WORKLOADS[name]
+    _say(f"[case] full workload {name} {w.shape_str()}")
+    d = make_inputs(w)
+    out, fin = gpu_run(gpu_lib, d, w.chunk)
+    Bsz, H = w.batch, w.nheads
+    pairs = sorted({(0, 0), (Bsz - 1, H - 1), (Bsz // 2, H // 2), (0, H - 1), (Bsz - 1, 1 % H),
+                    (Bsz // 3, (2 * H) // 3)})
+    for b, h in pairs:
+        s = _pair_slice(d, b, h, H, w.ngroups)
+        ref_out, ref_fin = oracle_run(s)
+        assert_close(out[b:b + 1, :, h:h + 1], ref_out, TOL["f16"], f"out (b={b}, h={h})")
+        assert_close(fin[b:b + 1, h:h + 1], ref_fin, TOL["f16"], f"final (b={b}, h={h})")
+    del d, out, fin
+    torch.cuda.empty_cache()
