@@ -106,34 +106,40 @@ def gpu_input_set(w: Workload, seed: int, device: str):
 
 def cpu_baseline(w: Workload, budget_s: float):
     """The fp64 oracle, as it stands, on this host's cores, over a bounded
-    sample of (b, h) sequences of the same workload, scaled to tokens/s of
-    the whole workload."""
+    sample of the same workload: whole (b, h) sequences, repeated until about
+    ``budget_s`` seconds of CPU work, scaled to tokens/s of the workload."""
     from oracle import oracle_max_threads, ssd_recurrence
     d = make_inputs(w)
     BH = w.batch * w.nheads
     all_pairs = [(b, h) for b in range(w.batch) for h in range(w.nheads)]
     threads = oracle_max_threads()
-    # probe with one pair per thread to size the sample
-    n = min(BH, max(1, threads))
-    t0 = time.perf_counter()
-    ssd_recurrence(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
-                   initial_states=d["initial_states"], dt_softplus=True, pairs=all_pairs[:n])
-    t_probe = time.perf_counter() - t0
-    per_pair = t_probe / n * threads if n >= threads else t_probe
-    n_pairs = int(min(BH, max(n, budget_s / max(per_pair, 1e-9) * threads)))
-    n_pairs = max(threads, (n_pairs // threads) * threads) if n_pairs >= threads else n_pairs
-    n_pairs = min(n_pairs, BH)
-    step = max(1, BH // n_pairs)
-    pairs = all_pairs[::step][:n_pairs]
-    t0 = time.perf_counter()
-    ssd_recurrence(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
-                   initial_states=d["initial_states"], dt_softplus=True, pairs=pairs)
-    t = time.perf_counter() - t0
-    frac = len(pairs) / BH
-    t_full = t / frac
+
+    def run(pairs):
+        t0 = time.perf_counter()
+        ssd_recurrence(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                       initial_states=d["initial_states"], dt_softplus=True, pairs=pairs)
+        return time.perf_counter() - t0
+
+    # probe: one sequence per thread (spread over the workload)
+    n = min(BH, threads)
+    stride = max(1, BH // n)
+    t_probe = run(all_pairs[::stride][:n])
+    per_round = t_probe                      # one round = `threads` sequences in parallel
+    rounds_full = math.ceil(BH / n)
+    t_full_est = per_round * rounds_full
+    if t_full_est <= budget_s:
+        pairs = all_pairs
+        reps = max(1, int(budget_s // max(t_full_est, 1e-6)))
+    else:
+        n_pairs = max(n, min(BH, int(budget_s / per_round) * n))
+        pairs = all_pairs[::max(1, BH // n_pairs)][:n_pairs]
+        reps = 1
+    t = sum(run(pairs) for _ in range(reps))
+    t_full = t / reps * BH / len(pairs)
     return {"value": w.tokens / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(pairs)} of {BH} (b,h) sequences of the full {w.shape_str()} workload "
-                      f"({t:.1f} s, fp64, {threads} OpenMP threads); scaled to all {BH}"}
+            "sample": f"{len(pairs)} of {BH} (b,h) sequences of the {w.shape_str()} workload, "
+                      f"{reps} repetition(s), {t:.1f} s of fp64 recurrence on {threads} OpenMP "
+                      f"threads; scaled to the whole workload"}
 
 
 def main(argv=None):
@@ -147,6 +153,9 @@ def main(argv=None):
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = auto)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="before warmup, run a plain device copy of this many MB three times "
+                         "(a known-size reference kernel for HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -180,6 +189,17 @@ def main(argv=None):
         calls.append(call)
     cpg, ngroups = ssd.plan(calls[0].desc, w.chunk)
     stream = torch.cuda.current_stream().cuda_stream
+
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {n * 4} bytes read + {n * 4} written per copy",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     for k in range(args.warmup):
         calls[k % n_sets].launch(stream)

@@ -37,7 +37,8 @@
 
 namespace {
 
-constexpr int kThreads = 256;   // 4 wave64s
+constexpr int kThreads = 512;   // 8 wave64s
+constexpr int kWaves = kThreads / 64;
 constexpr int kJB = 64;         // tokens per LDS-staged block
 constexpr int kP = 64;          // compiled head dim
 constexpr float kLog2e = 1.4426950408889634f;
@@ -75,13 +76,17 @@ __device__ __forceinline__ f32x4 mma(const f32x8 &a, const f32x8 &b, f32x4 c) {
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
-// ---------------------------------------------------------------- storage I/O
-struct IoF32 {
-  using raw = float;
-};
-struct IoBF16 {
-  using raw = uint16_t;
-};
+// ---------------------------------------------------------------- buffer access
+// Every tensor of one batch row is addressed through a raw buffer resource
+// (base in SGPRs, 32-bit byte offsets per lane).  The hardware range check
+// returns zeros for loads past the end of the row's data and drops stores
+// past it, which is how tokens beyond the sequence end are handled.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) {
   return __uint_as_float(v << 16);
@@ -95,40 +100,56 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
-template <class IO> __device__ __forceinline__ f32x4 load4(const void *base, int64_t idx);
-template <> __device__ __forceinline__ f32x4 load4<IoF32>(const void *base, int64_t idx) {
-  return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + idx);
-}
-template <> __device__ __forceinline__ f32x4 load4<IoBF16>(const void *base, int64_t idx) {
-  uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + idx);
-  f32x4 r;
-  r[0] = bf16_bits_to_f32(v.x & 0xffffu);
-  r[1] = bf16_bits_to_f32(v.x >> 16);
-  r[2] = bf16_bits_to_f32(v.y & 0xffffu);
-  r[3] = bf16_bits_to_f32(v.y >> 16);
-  return r;
-}
-
-template <class IO> __device__ __forceinline__ float load1(const void *base, int64_t idx);
-template <> __device__ __forceinline__ float load1<IoF32>(const void *base, int64_t idx) {
-  return static_cast<const float *>(base)[idx];
-}
-template <> __device__ __forceinline__ float load1<IoBF16>(const void *base, int64_t idx) {
-  return bf16_bits_to_f32(static_cast<const uint16_t *>(base)[idx]);
-}
-
-// Eight consecutive elements converted to the MMA operand type.
-template <class IO, bool F32>
-__device__ __forceinline__ typename Mma<F32>::frag load8(const void *base, int64_t idx) {
-  f32x4 lo = load4<IO>(base, idx), hi = load4<IO>(base, idx + 4);
-  typename Mma<F32>::frag r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = (typename Mma<F32>::T)lo[e];
-    r[4 + e] = (typename Mma<F32>::T)hi[e];
+// Storage formats of x, B, C (and z).  Loads are split into an issue step
+// (raw registers) and a convert step so a whole block's loads can be in
+// flight before any of them is used.  Offsets are in elements.
+struct IoF32 {
+  static constexpr int esz = 4;
+  using raw4 = f32x4;
+  struct raw8 {
+    f32x4 lo, hi;
+  };
+  static __device__ __forceinline__ raw4 load4(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off * 4, 0, 0));
   }
-  return r;
-}
+  static __device__ __forceinline__ raw8 load8(rsrc_t r, uint32_t off) {
+    return raw8{load4(r, off), load4(r, off + 4)};
+  }
+  static __device__ __forceinline__ f32x4 cvt4(const raw4 &v) { return v; }
+  static __device__ __forceinline__ float cvt8(const raw8 &v, int e) {
+    return e < 4 ? v.lo[e] : v.hi[e - 4];
+  }
+  static __device__ __forceinline__ float load1(rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off * 4, 0, 0));
+  }
+};
+
+struct IoBF16 {
+  static constexpr int esz = 2;
+  typedef unsigned int raw4 __attribute__((vector_size(8)));
+  typedef unsigned int raw8 __attribute__((vector_size(16)));
+  static __device__ __forceinline__ raw4 load4(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off * 2, 0, 0);
+  }
+  static __device__ __forceinline__ raw8 load8(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off * 2, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 cvt4(const raw4 &v) {
+    f32x4 o;
+    o[0] = bf16_bits_to_f32(v[0] & 0xffffu);
+    o[1] = bf16_bits_to_f32(v[0] >> 16);
+    o[2] = bf16_bits_to_f32(v[1] & 0xffffu);
+    o[3] = bf16_bits_to_f32(v[1] >> 16);
+    return o;
+  }
+  static __device__ __forceinline__ float cvt8(const raw8 &v, int e) {
+    const uint32_t w = v[e >> 1];
+    return bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xffffu));
+  }
+  static __device__ __forceinline__ float load1(rsrc_t r, uint32_t off) {
+    return bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off * 2, 0, 0));
+  }
+};
 
 // ---------------------------------------------------------------- parameters
 struct Params {
@@ -143,6 +164,8 @@ struct Params {
   const float *h0;
   void *out;
   float *final_state;
+  float2 *lamd;      // [B*H][nc][Q]: per token {Lam (log2, inclusive in-chunk), delta}
+  float2 *cinfo;     // [B*H][nc]: per chunk {Lam_end, 1 if the factored decay is safe}
   float *grp_state;  // [B*H][ngroups-1][P*N]: group aggregates, then entering states
   float *grp_lam;    // [B*H][ngroups-1]: group total log2-decay
   int64_t batch, L, H, G, nc, ngroups, cpg;
@@ -172,21 +195,55 @@ __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_her
   return true;
 }
 
-// chunk_cumsum for one chunk: discretise dt (softplus, clamp), then the
-// inclusive prefix of delta*A over the chunk, in log2 units.  Tokens past the
-// sequence end get delta = 0, so they decay nothing and add nothing.
-// Leaves Lam (log2) in sLam[0..Q) and delta in sDelta[0..Q); returns Lam_end.
+// Buffer resources and element offsets of one (b, h) sequence.
+template <int N, class IO>
+struct SeqView {
+  rsrc_t x, B, C;
+  uint32_t H, G, h, g;
+  __device__ __forceinline__ SeqView(const Params &p, int64_t b, int64_t h_, int64_t g_) {
+    const uint64_t L = (uint64_t)p.L;
+    H = (uint32_t)p.H;
+    G = (uint32_t)p.G;
+    h = (uint32_t)h_;
+    g = (uint32_t)g_;
+    const uint64_t lhp = L * p.H * kP, lgn = L * p.G * N;
+    x = make_rsrc(static_cast<const char *>(p.x) + b * lhp * IO::esz, (uint32_t)(lhp * IO::esz));
+    B = make_rsrc(static_cast<const char *>(p.B) + b * lgn * IO::esz, (uint32_t)(lgn * IO::esz));
+    C = make_rsrc(static_cast<const char *>(p.C) + b * lgn * IO::esz, (uint32_t)(lgn * IO::esz));
+  }
+  __device__ __forceinline__ uint32_t xoff(uint32_t t, uint32_t col) const { return (t * H + h) * kP + col; }
+  __device__ __forceinline__ uint32_t boff(uint32_t t, uint32_t col) const { return (t * G + g) * N + col; }
+};
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, then synchronises the workgroup.  Unlike __syncthreads it does
+// not drain outstanding global loads, so prefetched data stays in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// chunk_cumsum (its own kernel, ahead of the matrix passes): for one
+// (b, h, chunk), discretise dt (dt_bias, softplus, clamp), then the inclusive
+// in-chunk prefix Lam of delta*A in log2 units.  Tokens past the sequence end
+// get delta = 0, so they decay nothing and add nothing.  Writes {Lam, delta}
+// per token and {Lam_end, factored} per chunk, where factored says whether
+// |delta*A| <= 7 (log2 units) for every token of the chunk, which keeps the
+// factored intra-chunk decay of the main pass inside fp32 range.
 template <int Q>
-__device__ __forceinline__ float chunk_cumsum(const Params &p, int64_t b, int64_t h, int64_t t0,
-                                              int Qc, float A2, float bias, float *sLam,
-                                              float *sDelta, float *sWave) {
+__global__ __launch_bounds__(256) void ssd_chunk_cumsum_kernel(Params p) {
+  __shared__ float wave_sum[4];
+  __shared__ int wave_big[4];
+  const int64_t bhc = blockIdx.x;
+  const int64_t c = bhc % p.nc, bh = bhc / p.nc;
+  const int64_t b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t = c * Q + tid;
   float a = 0.f, delta = 0.f;
-  if (tid < Qc) {
-    float u = p.dt[(b * p.L + t0 + tid) * p.H + h] + bias;
-    if (p.dt_softplus) u = (u > 20.f) ? u : log1pf(expf(u));
+  if (t < p.L) {
+    float u = p.dt[(b * p.L + t) * p.H + h] + (p.dt_bias ? p.dt_bias[h] : 0.f);
+    if (p.dt_softplus) u = (u > 20.f) ? u : __logf(1.f + __expf(u));
     delta = fminf(fmaxf(u, p.dt_min), p.dt_max);
-    a = delta * A2;
+    a = delta * p.A[h] * kLog2e;
   }
   float v = a;
 #pragma unroll
@@ -194,83 +251,133 @@ __device__ __forceinline__ float chunk_cumsum(const Params &p, int64_t b, int64_
     const float nb = __shfl_up(v, off, 64);
     if (lane >= off) v += nb;
   }
-  if (lane == 63) sWave[wave] = v;
+  const uint64_t big = __ballot(fabsf(a) > 7.f);
+  if (lane == 63) wave_sum[wave] = v;
+  if (lane == 0) wave_big[wave] = big != 0;
   __syncthreads();
-  float pre = 0.f;
-  for (int w = 0; w < wave; ++w) pre += sWave[w];
-  v += pre;
-  if (tid < Q) {
-    sLam[tid] = v;
-    sDelta[tid] = delta;
+  float pre = 0.f, tot = 0.f;
+  int bigc = 0;
+#pragma unroll
+  for (int w = 0; w < Q / 64; ++w) {
+    tot += wave_sum[w];
+    pre += (w < wave) ? wave_sum[w] : 0.f;
+    bigc |= wave_big[w];
   }
-  __syncthreads();
-  return sLam[Q - 1];
+  p.lamd[bhc * Q + tid] = make_float2(v + pre, delta);
+  if (tid == 0) p.cinfo[bhc] = make_float2(tot, bigc ? 0.f : 1.f);
 }
 
-// Stage tokens [t0 + 64 jb, +64) of one chunk into LDS:
+// Per-chunk scalars in LDS (Lam in log2 units).
+//   lam[j]   inclusive in-chunk prefix of delta*A;  delta[j]
+//   w[j]     exp(Lam_end - Lam_j) delta_j      (chunk_state weights)
+//   u[j]     exp(Lam_m - Lam_j) delta_j, m the reference token (16th) of j's
+//            32-token sub-block; mid[j/32] = Lam_m
+template <int Q> struct ChunkLds {
+  float lam[Q], delta[Q], w[Q], u[Q], mid[Q / 32];
+};
+
+// This thread's {Lam, delta} record of a chunk (threads past Q load nothing).
+template <int Q>
+__device__ __forceinline__ float2 load_lamd(const Params &p, int64_t bh, int64_t c) {
+  const int tid = threadIdx.x;
+  if (Q < kThreads && tid >= Q) return make_float2(0.f, 0.f);
+  return p.lamd[(bh * p.nc + c) * Q + tid];
+}
+
+// Fill the chunk's LDS scalars from the prefetched records (caller puts a
+// barrier before any reader).
+template <int Q>
+__device__ __forceinline__ void chunk_prep(float2 ld, float lend2, ChunkLds<Q> &cl) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const float lam = ld.x, delta = ld.y;
+  const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 16));
+  const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 48));
+  const float mid = (lane < 32) ? m0 : m1;
+  if (tid < Q) {
+    cl.lam[tid] = lam;
+    cl.delta[tid] = delta;
+    cl.w[tid] = fast_exp2(lend2 - lam) * delta;
+    cl.u[tid] = fast_exp2(mid - lam) * delta;
+    if ((lane & 31) == 16) cl.mid[tid >> 5] = lam;
+  }
+}
+
+// Raw global data of one 64-token block: B rows [64][N] and x rows [64][P].
+// A loading thread holds 4 consecutive rows x 4 consecutive columns of B
+// and/or of x.  B takes 4N threads (all 512 when N = 128); x takes 256
+// threads (the upper half when N = 64, the lower half otherwise).
+template <int N, class IO>
+struct BlockRaw {
+  static constexpr int NG = N / 4;          // column groups of B
+  static constexpr int BTHREADS = 16 * NG;  // 16 row groups of 4 rows
+  static constexpr int XBASE = (BTHREADS == kThreads) ? 0 : BTHREADS;
+  typename IO::raw4 b[4];
+  typename IO::raw4 x[4];
+};
+
+// Issue the loads of block jb of the chunk starting at t0.
+template <int N, class IO>
+__device__ __forceinline__ void load_block(const SeqView<N, IO> &sv, uint32_t t0, int jb,
+                                           BlockRaw<N, IO> &r) {
+  using BR = BlockRaw<N, IO>;
+  const int tid = threadIdx.x;
+  if (tid < BR::BTHREADS) {
+    const int ng = tid % BR::NG, rg = tid / BR::NG;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r.b[e] = IO::load4(sv.B, sv.boff(t0 + kJB * jb + 4 * rg + e, 4 * ng));
+  }
+  const int xt = tid - BR::XBASE;
+  if (xt >= 0 && xt < 256) {
+    const int pg = xt % (kP / 4), rg = xt / (kP / 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r.x[e] = IO::load4(sv.x, sv.xoff(t0 + kJB * jb + 4 * rg + e, 4 * pg));
+  }
+}
+
+// Write a loaded block into LDS in the MMA operand type:
 //   sB  [64][N]  B rows            (A operand of B.C^T; only if WANT_B)
-//   sBT [N][64]  (w_j B_j)^T with w_j = exp(Lam_end - Lam_j) delta_j
+//   sBT [N][64]  (w_j B_j)^T
 //   sXT [P][64]  x^T
-// Each thread loads 4 rows x 4 columns and transposes them in registers.
 template <int N, bool F32, class IO, bool WANT_B>
-__device__ __forceinline__ void stage_block(const Params &p, int64_t b, int64_t h, int64_t g,
-                                            int64_t t0, int jb, int Qc, float lend2,
-                                            const float *sLam, const float *sDelta,
+__device__ __forceinline__ void store_block(const BlockRaw<N, IO> &r, int jb, const float *sw,
                                             typename Mma<F32>::T *sB, typename Mma<F32>::T *sBT,
                                             typename Mma<F32>::T *sXT) {
   using T = typename Mma<F32>::T;
   using quad = typename Mma<F32>::quad;
+  using BR = BlockRaw<N, IO>;
   constexpr int LDN = N + 8, LDJ = kJB + 8;
   const int tid = threadIdx.x;
-  // B block
-  {
-    constexpr int NG = N / 4;
-    constexpr int RG = kThreads / NG;
-    constexpr int PASSES = kJB / (4 * RG);
-    const int ng = tid % NG, rg = tid / NG;
-#pragma unroll
-    for (int pass = 0; pass < PASSES; ++pass) {
-      const int r0 = pass * 4 * RG + 4 * rg;
-      f32x4 v[4];
-      float wgt[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jl = kJB * jb + r0 + e;  // token within chunk
-        if (jl < Qc) {
-          v[e] = load4<IO>(p.B, ((b * p.L + t0 + jl) * p.G + g) * N + 4 * ng);
-          wgt[e] = fast_exp2(lend2 - sLam[jl]) * sDelta[jl];
-        } else {
-          v[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-          wgt[e] = 0.f;
-        }
-        if (WANT_B) {
-          quad q;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) q[c] = (T)v[e][c];
-          *reinterpret_cast<quad *>(&sB[(r0 + e) * LDN + 4 * ng]) = q;
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        quad q;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] = (T)(wgt[e] * v[e][c]);
-        *reinterpret_cast<quad *>(&sBT[(4 * ng + c) * LDJ + r0]) = q;
-      }
-    }
-  }
-  // x block
-  {
-    constexpr int PG = kP / 4;  // 16
-    const int pg = tid % PG, rg = tid / PG;  // rg in [0,16): rows 4rg..4rg+3
+  if (tid < BR::BTHREADS) {
+    const int ng = tid % BR::NG, rg = tid / BR::NG;
     const int r0 = 4 * rg;
+    const f32x4 wgt = *reinterpret_cast<const f32x4 *>(&sw[kJB * jb + r0]);
     f32x4 v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int jl = kJB * jb + r0 + e;
-      v[e] = (jl < Qc) ? load4<IO>(p.x, ((b * p.L + t0 + jl) * p.H + h) * kP + 4 * pg)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[e] = IO::cvt4(r.b[e]);
+      if (WANT_B) {
+        quad q;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[c] = (T)v[e][c];
+        *reinterpret_cast<quad *>(&sB[(r0 + e) * LDN + 4 * ng]) = q;
+      }
     }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      quad q;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = (T)(wgt[e] * v[e][c]);
+      *reinterpret_cast<quad *>(&sBT[(4 * ng + c) * LDJ + r0]) = q;
+    }
+  }
+  const int xt = tid - BR::XBASE;
+  if (xt >= 0 && xt < 256) {
+    const int pg = xt % (kP / 4), rg = xt / (kP / 4);
+    const int r0 = 4 * rg;
+    f32x4 v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = IO::cvt4(r.x[e]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       quad q;
@@ -281,92 +388,168 @@ __device__ __forceinline__ void stage_block(const Params &p, int64_t b, int64_t 
   }
 }
 
-// chunk_state on one staged block: wave w owns state rows p in [16w, 16w+16)
-// and all N columns; S += X^T diag(w) B over the block's 64 tokens.
+// The z gate of one 64-token block, staged like x so each row's epilogue
+// finds it in LDS: thread t holds row t/8, columns 8 (t%8) .. +8.
+typedef unsigned int u32x4v __attribute__((vector_size(16)));
+struct ZRaw {
+  u32x4v lo, hi;  // 8 fp32, or 8 bf16 in lo
+};
+
+__device__ __forceinline__ void load_z(rsrc_t rz, bool bf16, uint32_t H, uint32_t h, uint32_t t0,
+                                       int jb, ZRaw &r) {
+  const int tid = threadIdx.x;
+  const uint32_t off = ((t0 + kJB * jb + tid / 8) * H + h) * kP + 8 * (tid % 8);
+  if (bf16) {
+    r.lo = IoBF16::load8(rz, off);
+  } else {
+    r.lo = __builtin_amdgcn_raw_buffer_load_b128(rz, off * 4, 0, 0);
+    r.hi = __builtin_amdgcn_raw_buffer_load_b128(rz, off * 4 + 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void store_z(const ZRaw &r, bool bf16, float *sZ) {
+  constexpr int LDZ = kP + 4;
+  const int tid = threadIdx.x;
+  f32x4 lo, hi;
+  if (bf16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = IoBF16::cvt8(r.lo, e);
+      hi[e] = IoBF16::cvt8(r.lo, 4 + e);
+    }
+  } else {
+    lo = __builtin_bit_cast(f32x4, r.lo);
+    hi = __builtin_bit_cast(f32x4, r.hi);
+  }
+  float *dst = &sZ[(tid / 8) * LDZ + 8 * (tid % 8)];
+  *reinterpret_cast<f32x4 *>(dst) = lo;
+  *reinterpret_cast<f32x4 *>(dst + 4) = hi;
+}
+
+// chunk_state on one staged block.  Wave w owns state rows p in
+// [16 (w%4), +16) and columns n in [N/2 (w/4), +N/2): S += X^T diag(w) B over
+// the block's 64 tokens.
 template <int N, bool F32>
 __device__ __forceinline__ void state_block_mma(const typename Mma<F32>::T *sXT,
                                                 const typename Mma<F32>::T *sBT, f32x4 *sacc) {
   using frag = typename Mma<F32>::frag;
   constexpr int LDJ = kJB + 8;
+  constexpr int NN = N / 32;  // n-tiles per wave
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lq = lane >> 4;
-#pragma unroll
+  const int ps = w & 3, n0 = (w >> 2) * NN;
+#pragma unroll 1
   for (int kb = 0; kb < kJB / 32; ++kb) {
-    const frag a = *reinterpret_cast<const frag *>(&sXT[(16 * w + lr) * LDJ + 32 * kb + 8 * lq]);
+    const frag a = *reinterpret_cast<const frag *>(&sXT[(16 * ps + lr) * LDJ + 32 * kb + 8 * lq]);
 #pragma unroll
-    for (int nt = 0; nt < N / 16; ++nt) {
-      const frag bf = *reinterpret_cast<const frag *>(&sBT[(16 * nt + lr) * LDJ + 32 * kb + 8 * lq]);
-      sacc[nt] = mma(a, bf, sacc[nt]);
+    for (int t = 0; t < NN; ++t) {
+      const frag bf =
+          *reinterpret_cast<const frag *>(&sBT[(16 * (n0 + t) + lr) * LDJ + 32 * kb + 8 * lq]);
+      sacc[t] = mma(a, bf, sacc[t]);
     }
   }
 }
 
-// Row tiles (16 rows each) of a chunk owned by wave w.  With 8 or more tiles
-// a wave takes mirrored pairs (w, 7-w) of every 8, balancing the causal work.
-template <int Q>
-__device__ __forceinline__ int row_tile(int k, int w) {
-  constexpr int NT = Q / 16;
-  if (NT == 4) return w;
-  const int pi = k >> 1;
-  return (k & 1) ? 8 * pi + 7 - w : 8 * pi + w;
+// Row and column in [P][N] of element r of state tile t held by this lane.
+__device__ __forceinline__ int state_row(int r) {
+  return 16 * ((threadIdx.x >> 6) & 3) + 4 * ((threadIdx.x & 63) >> 4) + r;
 }
+template <int N>
+__device__ __forceinline__ int state_col(int t) {
+  return 16 * ((threadIdx.x >> 8) * (N / 32) + t) + (threadIdx.x & 15);
+}
+
+// Work split of a chunk's Q output rows over the 8 waves.  Waves w and w+4
+// share a SIMD; with 8 or 16 row tiles a SIMD gets mirrored tiles (s, 7-s,
+// 8+s, 15-s) so the causal work per SIMD is even.  With 4 row tiles (Q = 64)
+// the two waves of a SIMD split the head dim instead.
+template <int Q> struct RowSplit {
+  static constexpr int NT = Q / 16;
+  static constexpr int NR = NT == 16 ? 2 : 1;      // row tiles per wave
+  static constexpr int PT = NT == 4 ? 2 : 4;       // p-tiles per wave
+  static __device__ __forceinline__ int tile(int k, int w) {
+    const int s = w & 3, hf = w >> 2;
+    if (NT == 4) return s;
+    if (NT == 8) return hf ? 7 - s : s;
+    return hf ? (k ? 8 + s : 7 - s) : (k ? 15 - s : s);
+  }
+  static __device__ __forceinline__ int pt0(int w) { return NT == 4 ? 2 * (w >> 2) : 0; }
+};
+
+__device__ __forceinline__ int nblocks(int Qc) { return (Qc + kJB - 1) / kJB; }
 
 // ---------------------------------------------------------------- kernels
 
 // First pass (only when a sequence is split into several chunk groups): the
 // state each of the first ngroups-1 groups builds from a zero start, and the
-// group's total decay.
+// group's total decay.  Blocks of B and x are prefetched one ahead.
 template <int Q, int N, bool F32, class IO>
-__global__ __launch_bounds__(kThreads) void ssd_group_state_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, F32 ? 2 : 4) void ssd_group_state_kernel(Params p) {
   using T = typename Mma<F32>::T;
   constexpr int LDJ = kJB + 8;
+  constexpr int NN = N / 32;
   __shared__ __attribute__((aligned(16))) T sBT[N * LDJ];
   __shared__ __attribute__((aligned(16))) T sXT[kP * LDJ];
-  __shared__ float sLam[Q], sDelta[Q], sWave[4];
+  __shared__ __attribute__((aligned(16))) ChunkLds<Q> clb[2];
 
   int64_t b, h, j;
   if (!decode_tile(p, p.ngroups - 1, b, h, j)) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lq = lane >> 4;
   const int64_t g = h / (p.H / p.G);
-  const float A2 = p.A[h] * kLog2e;
-  const float bias = p.dt_bias ? p.dt_bias[h] : 0.f;
+  const int64_t bh = b * p.H + h;
+  const SeqView<N, IO> sv(p, b, h, g);
 
-  f32x4 sacc[N / 16];
+  f32x4 sacc[NN];
 #pragma unroll
-  for (int nt = 0; nt < N / 16; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NN; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float lgrp = 0.f;
   const int64_t c_begin = j * p.cpg, c_end = c_begin + p.cpg;  // never the last group
+  auto qc_of = [&](int64_t c) { return (int)((p.L - c * Q) < Q ? (p.L - c * Q) : Q); };
+
+  BlockRaw<N, IO> nxt;
+  load_block<N, IO>(sv, (uint32_t)(c_begin * Q), 0, nxt);
+  float2 ldv = load_lamd<Q>(p, bh, c_begin);
+  float2 civ = p.cinfo[bh * p.nc + c_begin];
   for (int64_t c = c_begin; c < c_end; ++c) {
-    const int64_t t0 = c * Q;
-    const int Qc = (int)((p.L - t0) < Q ? (p.L - t0) : Q);
-    const float lend2 = chunk_cumsum<Q>(p, b, h, t0, Qc, A2, bias, sLam, sDelta, sWave);
+    const uint32_t t0 = (uint32_t)(c * Q);
+    const int Qc = qc_of(c);
+    ChunkLds<Q> &cl = clb[c & 1];
+    const float lend2 = civ.x;
+    chunk_prep<Q>(ldv, lend2, cl);
+    if (c + 1 < c_end) {
+      ldv = load_lamd<Q>(p, bh, c + 1);
+      civ = p.cinfo[bh * p.nc + c + 1];
+    }
     const float dec = fast_exp2(lend2);
 #pragma unroll
-    for (int nt = 0; nt < N / 16; ++nt) sacc[nt] *= dec;
+    for (int t = 0; t < NN; ++t) sacc[t] *= dec;
     lgrp += lend2;
-    for (int jb = 0; jb < Q / kJB; ++jb) {
-      if (kJB * jb >= Qc) break;
-      __syncthreads();
-      stage_block<N, F32, IO, false>(p, b, h, g, t0, jb, Qc, lend2, sLam, sDelta, nullptr, sBT, sXT);
-      __syncthreads();
+    const int nb = nblocks(Qc);
+    for (int jb = 0; jb < nb; ++jb) {
+      lds_barrier();
+      store_block<N, F32, IO, false>(nxt, jb, cl.w, nullptr, sBT, sXT);
+      lds_barrier();
+      if (jb + 1 < nb)
+        load_block<N, IO>(sv, t0, jb + 1, nxt);
+      else if (c + 1 < c_end)
+        load_block<N, IO>(sv, t0 + Q, 0, nxt);
       state_block_mma<N, F32>(sXT, sBT, sacc);
     }
   }
-  const int64_t slot = (b * p.H + h) * (p.ngroups - 1) + j;
+  const int64_t slot = bh * (p.ngroups - 1) + j;
   float *dst = p.grp_state + slot * (int64_t)(kP * N);
 #pragma unroll
-  for (int nt = 0; nt < N / 16; ++nt)
+  for (int t = 0; t < NN; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(16 * w + 4 * lq + r) * N + 16 * nt + lr] = sacc[nt][r];
+    for (int r = 0; r < 4; ++r) dst[state_row(r) * N + state_col<N>(t)] = sacc[t][r];
   if (threadIdx.x == 0) p.grp_lam[slot] = lgrp;
 }
 
 // state_passing across chunk groups (elementwise over P*N, sequential over
 // groups): S = exp(Lam_grp) S + S_grp; slot j is overwritten with the state
 // entering group j+1.
-__global__ __launch_bounds__(kThreads) void ssd_group_passing_kernel(Params p, int PN) {
-  const int64_t blocks_per_bh = PN / kThreads;
+__global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p, int PN) {
+  const int64_t blocks_per_bh = PN / 256;
   const int64_t bh = blockIdx.x / blocks_per_bh;
-  const int64_t e = (blockIdx.x % blocks_per_bh) * kThreads + threadIdx.x;
+  const int64_t e = (blockIdx.x % blocks_per_bh) * 256 + threadIdx.x;
   float S = p.h0 ? p.h0[bh * PN + e] : 0.f;
   const int64_t ng1 = p.ngroups - 1;
   for (int64_t jj = 0; jj < ng1; ++jj) {
@@ -377,88 +560,126 @@ __global__ __launch_bounds__(kThreads) void ssd_group_passing_kernel(Params p, i
 }
 
 // Main pass: chunk_scan over the chunks of one group, carrying the state.
+// Per chunk: discretise + cumsum, inter-chunk term C.S_in^T from the carried
+// state, then per 64-token block the intra-chunk term and the block's
+// contribution to the carried state; the next block's loads are issued
+// before the current block's matrix work.
 template <int Q, int N, bool F32, class IO>
-__global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
   using T = typename Mma<F32>::T;
   using frag = typename Mma<F32>::frag;
   using quad = typename Mma<F32>::quad;
-  constexpr int NT = Q / 16;
-  constexpr int NR = (NT >= 4) ? NT / 4 : 1;  // row tiles per wave
-  constexpr int KB = N / 32;                  // K blocks over the state dim
+  using RS = RowSplit<Q>;
+  constexpr int NR = RS::NR, PT = RS::PT;
+  constexpr int KB = N / 32;  // K blocks over the state dim
+  constexpr int NN = N / 32;  // state n-tiles per wave
   constexpr int LDN = N + 8, LDJ = kJB + 8;
   __shared__ __attribute__((aligned(16))) T sB[kJB * LDN];
   __shared__ __attribute__((aligned(16))) T sBT[N * LDJ];
   __shared__ __attribute__((aligned(16))) T sXT[kP * LDJ];
   __shared__ __attribute__((aligned(16))) T sS[kP * LDN];
-  __shared__ float sLam[Q], sDelta[Q], sWave[4];
+  __shared__ __attribute__((aligned(16))) float sZ[kJB * (kP + 4)];
+  __shared__ __attribute__((aligned(16))) ChunkLds<Q> clb[2];
+  constexpr int LDZ = kP + 4;
 
   int64_t b, h, j;
   if (!decode_tile(p, p.ngroups, b, h, j)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lq = lane >> 4;
+  const int pt0 = RS::pt0(w);
   const int64_t g = h / (p.H / p.G);
-  const float A2 = p.A[h] * kLog2e;
-  const float bias = p.dt_bias ? p.dt_bias[h] : 0.f;
+  const SeqView<N, IO> sv(p, b, h, g);
+  const uint64_t lhp = (uint64_t)p.L * p.H * kP;
+  const int osz = p.out_bf16 ? 2 : 4, zsz = p.z_bf16 ? 2 : 4;
+  const rsrc_t rout = make_rsrc(static_cast<char *>(p.out) + b * lhp * osz, (uint32_t)(lhp * osz));
+  const rsrc_t rz = make_rsrc(p.z ? static_cast<const char *>(p.z) + b * lhp * zsz : nullptr,
+                              p.z ? (uint32_t)(lhp * zsz) : 0u);
   const float Dh = p.D ? p.D[h] : 0.f;
   const int64_t bh = b * p.H + h;
+  const int64_t c_begin = j * p.cpg;
+  const int64_t c_end = (c_begin + p.cpg < p.nc) ? c_begin + p.cpg : p.nc;
+  auto qc_of = [&](int64_t c) { return (int)((p.L - c * Q) < Q ? (p.L - c * Q) : Q); };
+
+  // prefetch registers: next 64-token block (and its z), next chunk's C rows
+  // and records
+  const bool has_z = p.z != nullptr, z_bf16 = p.z_bf16 != 0;
+  BlockRaw<N, IO> nxt;
+  ZRaw nz;
+  auto load_zb = [&](uint32_t t0, int jb) {
+    if (has_z) load_z(rz, z_bf16, sv.H, sv.h, t0, jb, nz);
+  };
+  load_block<N, IO>(sv, (uint32_t)(c_begin * Q), 0, nxt);
+  load_zb((uint32_t)(c_begin * Q), 0);
+  float2 ldv = load_lamd<Q>(p, bh, c_begin);
+  float2 civ = p.cinfo[bh * p.nc + c_begin];
+  typename IO::raw8 craw[NR][KB];
+  auto load_c = [&](uint32_t t0) {
+#pragma unroll
+    for (int k = 0; k < NR; ++k)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        craw[k][kb] = IO::load8(sv.C, sv.boff(t0 + 16 * RS::tile(k, w) + lr, 32 * kb + 8 * lq));
+  };
+  // C rows are prefetched during the previous chunk's last block when they
+  // fit in 16 registers, else loaded at the start of their chunk
+  constexpr bool kPrefetchC = NR * KB * sizeof(typename IO::raw8) <= 64;
+  if (kPrefetchC) load_c((uint32_t)(c_begin * Q));
 
   // state entering this group: h0 / zero for the first, the chained group
-  // state otherwise.  Wave w holds rows [16w, 16w+16), in accumulator layout.
-  f32x4 sacc[N / 16];
+  // state otherwise, in accumulator layout (see state_block_mma)
+  f32x4 sacc[NN];
   {
     const float *init = (j == 0) ? (p.h0 ? p.h0 + bh * (int64_t)(kP * N) : nullptr)
                                  : p.grp_state + (bh * (p.ngroups - 1) + (j - 1)) * (int64_t)(kP * N);
 #pragma unroll
-    for (int nt = 0; nt < N / 16; ++nt)
+    for (int t = 0; t < NN; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * w + 4 * lq + r, col = 16 * nt + lr;
-        sacc[nt][r] = init ? init[row * N + col] : 0.f;
-        sS[row * LDN + col] = (T)sacc[nt][r];
+        const int row = state_row(r), col = state_col<N>(t);
+        sacc[t][r] = init ? init[row * N + col] : 0.f;
+        sS[row * LDN + col] = (T)sacc[t][r];
       }
   }
 
-  const int64_t c_begin = j * p.cpg;
-  const int64_t c_end = (c_begin + p.cpg < p.nc) ? c_begin + p.cpg : p.nc;
   for (int64_t c = c_begin; c < c_end; ++c) {
-    const int64_t t0 = c * Q;
-    const int Qc = (int)((p.L - t0) < Q ? (p.L - t0) : Q);
-    const float lend2 = chunk_cumsum<Q>(p, b, h, t0, Qc, A2, bias, sLam, sDelta, sWave);
-
-    // C rows of this wave's tiles, in registers (B operand of B.C^T and A
-    // operand of C.S^T share one layout).
-    frag cfr[NR][KB];
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const int i = 16 * row_tile<Q>(k, w) + lr;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        if (i < Qc) {
-          cfr[k][kb] = load8<IO, F32>(p.C, ((b * p.L + t0 + i) * p.G + g) * N + 32 * kb + 8 * lq);
-        } else {
-#pragma unroll
-          for (int s = 0; s < 8; ++s) cfr[k][kb][s] = (T)0.f;
-        }
-      }
+    const uint32_t t0 = (uint32_t)(c * Q);
+    const int Qc = qc_of(c);
+    ChunkLds<Q> &cl = clb[c & 1];
+    if (!kPrefetchC) load_c(t0);
+    const float lend2 = civ.x;
+    const bool factored = civ.y != 0.f;
+    chunk_prep<Q>(ldv, lend2, cl);
+    lds_barrier();
+    if (c + 1 < c_end) {
+      ldv = load_lamd<Q>(p, bh, c + 1);
+      civ = p.cinfo[bh * p.nc + c + 1];
     }
 
+    // B operand of B.C^T and A operand of C.S^T share this layout
+    frag cfr[NR][KB];
+#pragma unroll
+    for (int k = 0; k < NR; ++k)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) cfr[k][kb][s] = (T)IO::cvt8(craw[k][kb], s);
+
     // inter-chunk term: Y = diag(exp(Lam)) C S_in^T
-    f32x4 yacc[NR][kP / 16];
+    f32x4 yacc[NR][PT];
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      const int row0 = 16 * row_tile<Q>(k, w);
-      float escale[4];
+      const int row0 = 16 * RS::tile(k, w);
+      const f32x4 lam4 = *reinterpret_cast<const f32x4 *>(&cl.lam[row0 + 4 * lq]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) escale[r] = fast_exp2(sLam[row0 + 4 * lq + r]);
-#pragma unroll
-      for (int pt = 0; pt < kP / 16; ++pt) {
+      for (int pt = 0; pt < PT; ++pt) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const frag sf = *reinterpret_cast<const frag *>(&sS[(16 * pt + lr) * LDN + 32 * kb + 8 * lq]);
+          const frag sf =
+              *reinterpret_cast<const frag *>(&sS[(16 * (pt0 + pt) + lr) * LDN + 32 * kb + 8 * lq]);
           acc = mma(cfr[k][kb], sf, acc);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= escale[r];
+        for (int r = 0; r < 4; ++r) acc[r] *= fast_exp2(lam4[r]);
         yacc[k][pt] = acc;
       }
     }
@@ -467,49 +688,96 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     {
       const float dec = fast_exp2(lend2);
 #pragma unroll
-      for (int nt = 0; nt < N / 16; ++nt) sacc[nt] *= dec;
+      for (int t = 0; t < NN; ++t) sacc[t] *= dec;
     }
 
-    for (int jb = 0; jb < Q / kJB; ++jb) {
-      if (kJB * jb >= Qc) break;
-      __syncthreads();
-      stage_block<N, F32, IO, true>(p, b, h, g, t0, jb, Qc, lend2, sLam, sDelta, sB, sBT, sXT);
-      __syncthreads();
-      // intra-chunk term for this wave's row tiles against tokens of block jb
+    const int nb = nblocks(Qc);
+    for (int jb = 0; jb < nb; ++jb) {
+      lds_barrier();
+      store_block<N, F32, IO, true>(nxt, jb, cl.w, sB, sBT, sXT);
+      if (has_z) store_z(nz, z_bf16, sZ);
+      lds_barrier();
+      if (jb + 1 < nb) {
+        load_block<N, IO>(sv, t0, jb + 1, nxt);
+        load_zb(t0, jb + 1);
+      } else if (c + 1 < c_end) {
+        load_block<N, IO>(sv, t0 + Q, 0, nxt);
+        load_zb(t0 + Q, 0);
+        if (kPrefetchC) load_c(t0 + Q);
+      }
+      // intra-chunk term for this wave's row tiles against tokens of block jb,
+      // one 32-token sub-block at a time (its B fragments serve every row
+      // tile of the wave that reaches it)
+#pragma unroll 1
+      for (int js = 0; js < kJB / 32; ++js) {
+        const int jbase = kJB * jb + 32 * js;
+        bool any = false;
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        const int rt = row_tile<Q>(k, w);
-        if (16 * rt + 15 < kJB * jb) continue;
-        const int i = 16 * rt + lr;
-        const float li = sLam[i];
+        for (int k = 0; k < NR; ++k) any |= jbase <= 16 * RS::tile(k, w) + 15;
+        if (!any) continue;
+        frag a0[KB], a1[KB];
 #pragma unroll
-        for (int js = 0; js < kJB / 32; ++js) {
-          const int jbase = kJB * jb + 32 * js;
-          if (jbase > 16 * rt + 15) break;
+        for (int kb = 0; kb < KB; ++kb) {
+          a0[kb] = *reinterpret_cast<const frag *>(&sB[(32 * js + lr) * LDN + 32 * kb + 8 * lq]);
+          a1[kb] = *reinterpret_cast<const frag *>(&sB[(32 * js + 16 + lr) * LDN + 32 * kb + 8 * lq]);
+        }
+        const int ja0 = jbase + 4 * lq;
+        const float lmid = cl.mid[jbase >> 5];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          const int row0 = 16 * RS::tile(k, w);
+          if (jbase > row0 + 15) continue;
+          const int i = row0 + lr;
+          const float li = cl.lam[i];
           // G^T[j][i] = B_j . C_i for j in [jbase, jbase+32), two 16x16 tiles
           f32x4 g0 = f32x4{0.f, 0.f, 0.f, 0.f}, g1 = g0;
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
-            const frag a0 = *reinterpret_cast<const frag *>(&sB[(32 * js + lr) * LDN + 32 * kb + 8 * lq]);
-            const frag a1 = *reinterpret_cast<const frag *>(&sB[(32 * js + 16 + lr) * LDN + 32 * kb + 8 * lq]);
-            g0 = mma(a0, cfr[k][kb], g0);
-            g1 = mma(a1, cfr[k][kb], g1);
+            g0 = mma(a0[kb], cfr[k][kb], g0);
+            g1 = mma(a1[kb], cfr[k][kb], g1);
           }
           // M[i][j] = G[i][j] exp(Lam_i - Lam_j) delta_j (j <= i), held as the
           // A operand of M.X: lane keeps row i, K slots j = jbase+4lq+r and
-          // jbase+16+4lq+r.
-          frag mf;
+          // jbase+16+4lq+r.  The decay factors as exp(Lam_i - Lam_m) times
+          // exp(Lam_m - Lam_j) delta_j with m the sub-block's reference token.
+          float ma[4], mc[4];
+          if (factored) {
+            const float vi = fast_exp2(li - lmid);
+            const f32x4 ua = *reinterpret_cast<const f32x4 *>(&cl.u[ja0]);
+            const f32x4 uc = *reinterpret_cast<const f32x4 *>(&cl.u[ja0 + 16]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int ja = jbase + 4 * lq + r, jc = ja + 16;
-            const float ma = g0[r] * fast_exp2(li - sLam[ja]) * sDelta[ja];
-            const float mc = g1[r] * fast_exp2(li - sLam[jc]) * sDelta[jc];
-            mf[r] = (T)(ja <= i ? ma : 0.f);
-            mf[4 + r] = (T)(jc <= i ? mc : 0.f);
+            for (int r = 0; r < 4; ++r) {
+              ma[r] = g0[r] * ua[r] * vi;
+              mc[r] = g1[r] * uc[r] * vi;
+            }
+          } else {
+            const f32x4 la = *reinterpret_cast<const f32x4 *>(&cl.lam[ja0]);
+            const f32x4 lc = *reinterpret_cast<const f32x4 *>(&cl.lam[ja0 + 16]);
+            const f32x4 da = *reinterpret_cast<const f32x4 *>(&cl.delta[ja0]);
+            const f32x4 dc = *reinterpret_cast<const f32x4 *>(&cl.delta[ja0 + 16]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              ma[r] = g0[r] * (fast_exp2(li - la[r]) * da[r]);
+              mc[r] = g1[r] * (fast_exp2(li - lc[r]) * dc[r]);
+            }
+          }
+          frag mf;
+          if (jbase + 31 > row0) {  // the sub-block meets the diagonal: mask j > i
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              mf[r] = (T)(ja0 + r <= i ? ma[r] : 0.f);
+              mf[4 + r] = (T)(ja0 + 16 + r <= i ? mc[r] : 0.f);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              mf[r] = (T)ma[r];
+              mf[4 + r] = (T)mc[r];
+            }
           }
 #pragma unroll
-          for (int pt = 0; pt < kP / 16; ++pt) {
-            const T *xrow = &sXT[(16 * pt + lr) * LDJ + 32 * js + 4 * lq];
+          for (int pt = 0; pt < PT; ++pt) {
+            const T *xrow = &sXT[(16 * (pt0 + pt) + lr) * LDJ + 32 * js + 4 * lq];
             const quad lo = *reinterpret_cast<const quad *>(xrow);
             const quad hi = *reinterpret_cast<const quad *>(xrow + 16);
             frag xb;
@@ -524,48 +792,52 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
       }
       // chunk_state contribution of this block to the carried state
       state_block_mma<N, F32>(sXT, sBT, sacc);
-    }
 
-    // epilogue: + D x, gate, store
+      // epilogue of the row tiles that lie in this block (their sums are
+      // complete): + D x with x from the staged block, the z gate from the
+      // staged z, store (rows past the sequence end are dropped by the buffer
+      // range check)
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const int row0 = 16 * row_tile<Q>(k, w);
+      for (int k = 0; k < NR; ++k) {
+        const int row0 = 16 * RS::tile(k, w);
+        if ((row0 >> 6) != jb) continue;
+        const int lrow = row0 - kJB * jb + 4 * lq;  // row within the block, + r
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = row0 + 4 * lq + r;
-        if (i >= Qc) continue;
-        const int64_t base = ((b * p.L + t0 + i) * p.H + h) * kP;
+        for (int pt = 0; pt < PT; ++pt) {
+          const int col = 16 * (pt0 + pt) + lr;
+          const quad xq = *reinterpret_cast<const quad *>(&sXT[col * LDJ + lrow]);
 #pragma unroll
-        for (int pt = 0; pt < kP / 16; ++pt) {
-          const int64_t idx = base + 16 * pt + lr;
-          float y = yacc[k][pt][r];
-          if (p.D) y += Dh * load1<IO>(p.x, idx);
-          if (p.z) {
-            const float zz = p.z_bf16 ? load1<IoBF16>(p.z, idx) : load1<IoF32>(p.z, idx);
-            y *= zz / (1.f + expf(-zz));
+          for (int r = 0; r < 4; ++r) {
+            float y = yacc[k][pt][r] + Dh * (float)xq[r];
+            if (has_z) {
+              const float zz = sZ[(lrow + r) * LDZ + col];
+              y *= zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz));
+            }
+            const uint32_t off = sv.xoff(t0 + kJB * jb + lrow + r, col);
+            if (p.out_bf16)
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(y), rout, off * 2, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rout, off * 4, 0, 0);
           }
-          if (p.out_bf16)
-            static_cast<uint16_t *>(p.out)[idx] = f32_to_bf16_bits(y);
-          else
-            static_cast<float *>(p.out)[idx] = y;
         }
       }
     }
 
-    // the state entering the next chunk, as the C.S^T operand
+    // the state entering the next chunk, as the C.S^T operand (all waves
+    // finished reading sS before the block loop's barriers)
 #pragma unroll
-    for (int nt = 0; nt < N / 16; ++nt)
+    for (int t = 0; t < NN; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        sS[(16 * w + 4 * lq + r) * LDN + 16 * nt + lr] = (T)sacc[nt][r];
+        sS[state_row(r) * LDN + state_col<N>(t)] = (T)sacc[t][r];
   }
 
   if (p.ret_final && j == p.ngroups - 1) {
     float *dst = p.final_state + bh * (int64_t)(kP * N);
 #pragma unroll
-    for (int nt = 0; nt < N / 16; ++nt)
+    for (int t = 0; t < NN; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * w + 4 * lq + r) * N + 16 * nt + lr] = sacc[nt][r];
+      for (int r = 0; r < 4; ++r) dst[state_row(r) * N + state_col<N>(t)] = sacc[t][r];
   }
 }
 
@@ -576,9 +848,13 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool is_supported_chunk(int64_t q) { return q == 64 || q == 128 || q == 256; }
 
+// Workspace: per-token {Lam, delta} records and per-chunk {Lam_end, flag}
+// written by chunk_cumsum, then (with several chunk groups) the group states
+// and group decays.
 struct Plan {
   int64_t nc, cpg, ngroups;
-  size_t state_bytes, lam_bytes;
+  size_t lamd_bytes, cinfo_bytes, state_bytes, lam_bytes;
+  size_t total() const { return lamd_bytes + cinfo_bytes + state_bytes + lam_bytes; }
 };
 
 // Validation of everything but pointers.
@@ -602,8 +878,13 @@ ssd_status check_shape(const ssd_desc *d, int64_t chunk) {
   if (d->headdim != kP) return SSD_ERR_UNSUPPORTED;
   if (d->dstate != 64 && d->dstate != 128) return SSD_ERR_UNSUPPORTED;
   if (!is_supported_chunk(chunk)) return SSD_ERR_UNSUPPORTED;
-  // 32-bit grid and 64-bit index headroom
+  // 32-bit grid; each batch row's x/z/out and B/C slices are addressed with
+  // 32-bit byte offsets
   if (d->batch > (1 << 20) || d->nheads > (1 << 20) || d->seqlen > ((int64_t)1 << 31))
+    return SSD_ERR_UNSUPPORTED;
+  const int64_t row_limit = (int64_t)1 << 31;
+  if (d->seqlen * d->nheads * d->headdim * 4 >= row_limit ||
+      d->seqlen * d->ngroups * d->dstate * 4 >= row_limit)
     return SSD_ERR_UNSUPPORTED;
   return SSD_OK;
 }
@@ -629,6 +910,8 @@ Plan make_plan(const ssd_desc *d, int64_t chunk) {
   pl.cpg = cpg;
   pl.ngroups = (pl.nc + cpg - 1) / cpg;
   const int64_t slots = bh * (pl.ngroups - 1);
+  pl.lamd_bytes = align_up((size_t)(bh * pl.nc * chunk) * 2 * sizeof(float));
+  pl.cinfo_bytes = align_up((size_t)(bh * pl.nc) * 2 * sizeof(float));
   pl.state_bytes = align_up((size_t)slots * (size_t)(d->headdim * d->dstate) * sizeof(float));
   pl.lam_bytes = align_up((size_t)slots * sizeof(float));
   if (slots == 0) pl.state_bytes = pl.lam_bytes = 0;
@@ -640,14 +923,16 @@ bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 template <int Q, int N, bool F32, class IO>
 ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, const ssd_desc *d) {
   const int64_t bh = prm.batch * prm.H;
+  hipLaunchKernelGGL(ssd_chunk_cumsum_kernel<Q>, dim3((unsigned)(bh * pl.nc)), dim3(Q), 0, stream,
+                     prm);
   if (pl.ngroups > 1) {
     const int64_t t1 = bh * (pl.ngroups - 1);
     const int64_t g1 = 8 * ((t1 + 7) / 8);
     hipLaunchKernelGGL((ssd_group_state_kernel<Q, N, F32, IO>), dim3((unsigned)g1), dim3(kThreads),
                        0, stream, prm);
     const int PN = kP * N;
-    hipLaunchKernelGGL(ssd_group_passing_kernel, dim3((unsigned)(bh * (PN / kThreads))),
-                       dim3(kThreads), 0, stream, prm, PN);
+    hipLaunchKernelGGL(ssd_group_passing_kernel, dim3((unsigned)(bh * (PN / 256))), dim3(256), 0,
+                       stream, prm, PN);
   }
   const int64_t t2 = bh * pl.ngroups;
   const int64_t g2 = 8 * ((t2 + 7) / 8);
@@ -706,7 +991,7 @@ ssd_status ssd_fwd_workspace_size(const ssd_desc *d, int64_t chunk, size_t *byte
   const ssd_status st = check_shape(d, chunk);
   if (st != SSD_OK) return st;
   const Plan pl = make_plan(d, chunk);
-  *bytes = pl.state_bytes + pl.lam_bytes;
+  *bytes = pl.total();
   return SSD_OK;
 }
 
@@ -733,8 +1018,8 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B
       (return_final_state && !aligned16(final_state)))
     return SSD_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, chunk);
-  const size_t need = pl.state_bytes + pl.lam_bytes;
-  if (need > 0 && (!d->workspace || d->workspace_bytes < need || !aligned16(d->workspace)))
+  const size_t need = pl.total();
+  if (!d->workspace || d->workspace_bytes < need || !aligned16(d->workspace))
     return SSD_ERR_WORKSPACE;
 
   Params prm;
@@ -750,9 +1035,12 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B
   prm.h0 = d->initial_state;
   prm.out = out;
   prm.final_state = final_state;
-  prm.grp_state = need > 0 ? static_cast<float *>(d->workspace) : nullptr;
-  prm.grp_lam = need > 0 ? reinterpret_cast<float *>(static_cast<char *>(d->workspace) + pl.state_bytes)
-                         : nullptr;
+  char *ws = static_cast<char *>(d->workspace);
+  prm.lamd = reinterpret_cast<float2 *>(ws);
+  prm.cinfo = reinterpret_cast<float2 *>(ws + pl.lamd_bytes);
+  prm.grp_state = pl.state_bytes ? reinterpret_cast<float *>(ws + pl.lamd_bytes + pl.cinfo_bytes) : nullptr;
+  prm.grp_lam = pl.lam_bytes ? reinterpret_cast<float *>(ws + pl.lamd_bytes + pl.cinfo_bytes + pl.state_bytes)
+                             : nullptr;
   prm.batch = d->batch;
   prm.L = d->seqlen;
   prm.H = d->nheads;
