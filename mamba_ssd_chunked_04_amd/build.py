@@ -23,7 +23,7 @@ def hipcc_command(out_path: str = LIB, extra=()) -> list:
     hipcc = os.environ.get("HIPCC", "hipcc")
     return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(REPO_DIR, "include"), SRC, "-o", out_path, *extra]
+            "-Wno-pass-failed", "-I", os.path.join(REPO_DIR, "include"), SRC, "-o", out_path, *extra]
 
 
 def build_library(verbose: bool = True) -> str:

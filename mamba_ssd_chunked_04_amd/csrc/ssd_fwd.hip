@@ -37,8 +37,6 @@
 
 namespace {
 
-constexpr int kThreads = 512;   // 8 wave64s
-constexpr int kWaves = kThreads / 64;
 constexpr int kJB = 64;         // tokens per LDS-staged block
 constexpr int kP = 64;          // compiled head dim
 constexpr float kLog2e = 1.4426950408889634f;
@@ -277,10 +275,10 @@ template <int Q> struct ChunkLds {
 };
 
 // This thread's {Lam, delta} record of a chunk (threads past Q load nothing).
-template <int Q>
+template <int Q, int T>
 __device__ __forceinline__ float2 load_lamd(const Params &p, int64_t bh, int64_t c) {
   const int tid = threadIdx.x;
-  if (Q < kThreads && tid >= Q) return make_float2(0.f, 0.f);
+  if (Q < T && tid >= Q) return make_float2(0.f, 0.f);
   return p.lamd[(bh * p.nc + c) * Q + tid];
 }
 
@@ -302,36 +300,44 @@ __device__ __forceinline__ void chunk_prep(float2 ld, float lend2, ChunkLds<Q> &
   }
 }
 
-// Raw global data of one 64-token block: B rows [64][N] and x rows [64][P].
-// A loading thread holds 4 consecutive rows x 4 consecutive columns of B
-// and/or of x.  B takes 4N threads (all 512 when N = 128); x takes 256
-// threads (the upper half when N = 64, the lower half otherwise).
-template <int N, class IO>
+// Raw global data of one 64-token block: B rows [64][N] and x rows [64][P],
+// spread over the workgroup's T threads in units of 4 rows x 4 columns.
+template <int N, class IO, int T>
 struct BlockRaw {
-  static constexpr int NG = N / 4;          // column groups of B
-  static constexpr int BTHREADS = 16 * NG;  // 16 row groups of 4 rows
-  static constexpr int XBASE = (BTHREADS == kThreads) ? 0 : BTHREADS;
-  typename IO::raw4 b[4];
-  typename IO::raw4 x[4];
+  static constexpr int NG = N / 4;                  // column groups of B
+  static constexpr int UB = 16 * NG;                // B units
+  static constexpr int UX = 16 * (kP / 4);          // x units
+  static constexpr int KB_ = (UB + T - 1) / T;      // B units per thread
+  static constexpr int KX = (UX + T - 1) / T;       // x units per thread
+  typename IO::raw4 b[KB_][4];
+  typename IO::raw4 x[KX][4];
 };
 
 // Issue the loads of block jb of the chunk starting at t0.
-template <int N, class IO>
+template <int N, class IO, int T>
 __device__ __forceinline__ void load_block(const SeqView<N, IO> &sv, uint32_t t0, int jb,
-                                           BlockRaw<N, IO> &r) {
-  using BR = BlockRaw<N, IO>;
+                                           BlockRaw<N, IO, T> &r) {
+  using BR = BlockRaw<N, IO, T>;
   const int tid = threadIdx.x;
-  if (tid < BR::BTHREADS) {
-    const int ng = tid % BR::NG, rg = tid / BR::NG;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      r.b[e] = IO::load4(sv.B, sv.boff(t0 + kJB * jb + 4 * rg + e, 4 * ng));
+  for (int k = 0; k < BR::KB_; ++k) {
+    const int u = tid + T * k;
+    if (u < BR::UB) {
+      const int ng = u % BR::NG, rg = u / BR::NG;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        r.b[k][e] = IO::load4(sv.B, sv.boff(t0 + kJB * jb + 4 * rg + e, 4 * ng));
+    }
   }
-  const int xt = tid - BR::XBASE;
-  if (xt >= 0 && xt < 256) {
-    const int pg = xt % (kP / 4), rg = xt / (kP / 4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r.x[e] = IO::load4(sv.x, sv.xoff(t0 + kJB * jb + 4 * rg + e, 4 * pg));
+  for (int k = 0; k < BR::KX; ++k) {
+    const int u = tid + T * k;
+    if (u < BR::UX) {
+      const int pg = u % (kP / 4), rg = u / (kP / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        r.x[k][e] = IO::load4(sv.x, sv.xoff(t0 + kJB * jb + 4 * rg + e, 4 * pg));
+    }
   }
 }
 
@@ -339,102 +345,132 @@ __device__ __forceinline__ void load_block(const SeqView<N, IO> &sv, uint32_t t0
 //   sB  [64][N]  B rows            (A operand of B.C^T; only if WANT_B)
 //   sBT [N][64]  (w_j B_j)^T
 //   sXT [P][64]  x^T
-template <int N, bool F32, class IO, bool WANT_B>
-__device__ __forceinline__ void store_block(const BlockRaw<N, IO> &r, int jb, const float *sw,
+template <int N, bool F32, class IO, int T, bool WANT_B>
+__device__ __forceinline__ void store_block(const BlockRaw<N, IO, T> &r, int jb, const float *sw,
                                             typename Mma<F32>::T *sB, typename Mma<F32>::T *sBT,
                                             typename Mma<F32>::T *sXT) {
-  using T = typename Mma<F32>::T;
+  using E = typename Mma<F32>::T;
   using quad = typename Mma<F32>::quad;
-  using BR = BlockRaw<N, IO>;
+  using BR = BlockRaw<N, IO, T>;
   constexpr int LDN = N + 8, LDJ = kJB + 8;
   const int tid = threadIdx.x;
-  if (tid < BR::BTHREADS) {
-    const int ng = tid % BR::NG, rg = tid / BR::NG;
-    const int r0 = 4 * rg;
-    const f32x4 wgt = *reinterpret_cast<const f32x4 *>(&sw[kJB * jb + r0]);
-    f32x4 v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = IO::cvt4(r.b[e]);
-      if (WANT_B) {
+  for (int k = 0; k < BR::KB_; ++k) {
+    const int u = tid + T * k;
+    if (u < BR::UB) {
+      const int ng = u % BR::NG, rg = u / BR::NG;
+      const int r0 = 4 * rg;
+      const f32x4 wgt = *reinterpret_cast<const f32x4 *>(&sw[kJB * jb + r0]);
+      f32x4 v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = IO::cvt4(r.b[k][e]);
+        if (WANT_B) {
+          quad q;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) q[c] = (E)v[e][c];
+          *reinterpret_cast<quad *>(&sB[(r0 + e) * LDN + 4 * ng]) = q;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
         quad q;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) q[c] = (T)v[e][c];
-        *reinterpret_cast<quad *>(&sB[(r0 + e) * LDN + 4 * ng]) = q;
+        for (int e = 0; e < 4; ++e) q[e] = (E)(wgt[e] * v[e][c]);
+        *reinterpret_cast<quad *>(&sBT[(4 * ng + c) * LDJ + r0]) = q;
       }
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      quad q;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) q[e] = (T)(wgt[e] * v[e][c]);
-      *reinterpret_cast<quad *>(&sBT[(4 * ng + c) * LDJ + r0]) = q;
-    }
   }
-  const int xt = tid - BR::XBASE;
-  if (xt >= 0 && xt < 256) {
-    const int pg = xt % (kP / 4), rg = xt / (kP / 4);
-    const int r0 = 4 * rg;
-    f32x4 v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = IO::cvt4(r.x[e]);
+  for (int k = 0; k < BR::KX; ++k) {
+    const int u = tid + T * k;
+    if (u < BR::UX) {
+      const int pg = u % (kP / 4), rg = u / (kP / 4);
+      const int r0 = 4 * rg;
+      f32x4 v[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      quad q;
+      for (int e = 0; e < 4; ++e) v[e] = IO::cvt4(r.x[k][e]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q[e] = (T)v[e][c];
-      *reinterpret_cast<quad *>(&sXT[(4 * pg + c) * LDJ + r0]) = q;
+      for (int c = 0; c < 4; ++c) {
+        quad q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = (E)v[e][c];
+        *reinterpret_cast<quad *>(&sXT[(4 * pg + c) * LDJ + r0]) = q;
+      }
     }
   }
 }
 
 // The z gate of one 64-token block, staged like x so each row's epilogue
-// finds it in LDS: thread t holds row t/8, columns 8 (t%8) .. +8.
+// finds it in LDS: unit u holds row u/8, columns 8 (u%8) .. +8.
 typedef unsigned int u32x4v __attribute__((vector_size(16)));
+template <int T>
 struct ZRaw {
-  u32x4v lo, hi;  // 8 fp32, or 8 bf16 in lo
+  static constexpr int K = 512 / T;
+  u32x4v lo[K], hi[K];  // 8 fp32, or 8 bf16 in lo
 };
 
+template <int T>
 __device__ __forceinline__ void load_z(rsrc_t rz, bool bf16, uint32_t H, uint32_t h, uint32_t t0,
-                                       int jb, ZRaw &r) {
-  const int tid = threadIdx.x;
-  const uint32_t off = ((t0 + kJB * jb + tid / 8) * H + h) * kP + 8 * (tid % 8);
-  if (bf16) {
-    r.lo = IoBF16::load8(rz, off);
-  } else {
-    r.lo = __builtin_amdgcn_raw_buffer_load_b128(rz, off * 4, 0, 0);
-    r.hi = __builtin_amdgcn_raw_buffer_load_b128(rz, off * 4 + 16, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void store_z(const ZRaw &r, bool bf16, float *sZ) {
-  constexpr int LDZ = kP + 4;
-  const int tid = threadIdx.x;
-  f32x4 lo, hi;
-  if (bf16) {
+                                       int jb, ZRaw<T> &r) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lo[e] = IoBF16::cvt8(r.lo, e);
-      hi[e] = IoBF16::cvt8(r.lo, 4 + e);
+  for (int k = 0; k < ZRaw<T>::K; ++k) {
+    const int u = threadIdx.x + T * k;
+    const uint32_t off = ((t0 + kJB * jb + u / 8) * H + h) * kP + 8 * (u % 8);
+    if (bf16) {
+      r.lo[k] = IoBF16::load8(rz, off);
+    } else {
+      r.lo[k] = __builtin_amdgcn_raw_buffer_load_b128(rz, off * 4, 0, 0);
+      r.hi[k] = __builtin_amdgcn_raw_buffer_load_b128(rz, off * 4 + 16, 0, 0);
     }
-  } else {
-    lo = __builtin_bit_cast(f32x4, r.lo);
-    hi = __builtin_bit_cast(f32x4, r.hi);
   }
-  float *dst = &sZ[(tid / 8) * LDZ + 8 * (tid % 8)];
-  *reinterpret_cast<f32x4 *>(dst) = lo;
-  *reinterpret_cast<f32x4 *>(dst + 4) = hi;
 }
 
-// chunk_state on one staged block.  Wave w owns state rows p in
-// [16 (w%4), +16) and columns n in [N/2 (w/4), +N/2): S += X^T diag(w) B over
-// the block's 64 tokens.
-template <int N, bool F32>
+template <int T>
+__device__ __forceinline__ void store_z(const ZRaw<T> &r, bool bf16, float *sZ) {
+  constexpr int LDZ = kP + 4;
+#pragma unroll
+  for (int k = 0; k < ZRaw<T>::K; ++k) {
+    const int u = threadIdx.x + T * k;
+    f32x4 lo, hi;
+    if (bf16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = IoBF16::cvt8(r.lo[k], e);
+        hi[e] = IoBF16::cvt8(r.lo[k], 4 + e);
+      }
+    } else {
+      lo = __builtin_bit_cast(f32x4, r.lo[k]);
+      hi = __builtin_bit_cast(f32x4, r.hi[k]);
+    }
+    float *dst = &sZ[(u / 8) * LDZ + 8 * (u % 8)];
+    *reinterpret_cast<f32x4 *>(dst) = lo;
+    *reinterpret_cast<f32x4 *>(dst + 4) = hi;
+  }
+}
+
+// Ownership of the P x N state by the W waves: wave w holds rows p in
+// [16 (w%4), +16) and NN = N/(4W/4... ) consecutive 16-column tiles starting
+// at tile (w/4) NN, in MFMA accumulator layout.
+template <int N, int W>
+struct StateSplit {
+  static constexpr int NN = (N / 16) / (W / 4);  // n-tiles per wave
+  static __device__ __forceinline__ int row(int r) {
+    return 16 * ((threadIdx.x >> 6) & 3) + 4 * ((threadIdx.x & 63) >> 4) + r;
+  }
+  static __device__ __forceinline__ int col(int t) {
+    return 16 * ((threadIdx.x >> 8) * NN + t) + (threadIdx.x & 15);
+  }
+};
+
+// chunk_state on one staged block: S += X^T diag(w) B over the block's 64
+// tokens, for this wave's share of the state.
+template <int N, bool F32, int W>
 __device__ __forceinline__ void state_block_mma(const typename Mma<F32>::T *sXT,
                                                 const typename Mma<F32>::T *sBT, f32x4 *sacc) {
   using frag = typename Mma<F32>::frag;
   constexpr int LDJ = kJB + 8;
-  constexpr int NN = N / 32;  // n-tiles per wave
+  constexpr int NN = StateSplit<N, W>::NN;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lq = lane >> 4;
   const int ps = w & 3, n0 = (w >> 2) * NN;
 #pragma unroll 1
@@ -449,30 +485,28 @@ __device__ __forceinline__ void state_block_mma(const typename Mma<F32>::T *sXT,
   }
 }
 
-// Row and column in [P][N] of element r of state tile t held by this lane.
-__device__ __forceinline__ int state_row(int r) {
-  return 16 * ((threadIdx.x >> 6) & 3) + 4 * ((threadIdx.x & 63) >> 4) + r;
-}
-template <int N>
-__device__ __forceinline__ int state_col(int t) {
-  return 16 * ((threadIdx.x >> 8) * (N / 32) + t) + (threadIdx.x & 15);
-}
-
-// Work split of a chunk's Q output rows over the 8 waves.  Waves w and w+4
-// share a SIMD; with 8 or 16 row tiles a SIMD gets mirrored tiles (s, 7-s,
-// 8+s, 15-s) so the causal work per SIMD is even.  With 4 row tiles (Q = 64)
-// the two waves of a SIMD split the head dim instead.
-template <int Q> struct RowSplit {
+// Work split of a chunk's Q output rows (NT = Q/16 row tiles) over W waves.
+// Row tiles are dealt in mirrored sets (s, 7-s, 8+s, 15-s, ...) so the
+// causal work per SIMD is even; with fewer tiles than waves the waves
+// sharing a SIMD split the head dim instead.
+template <int Q, int W>
+struct RowSplit {
   static constexpr int NT = Q / 16;
-  static constexpr int NR = NT == 16 ? 2 : 1;      // row tiles per wave
-  static constexpr int PT = NT == 4 ? 2 : 4;       // p-tiles per wave
+  static constexpr int NR = NT >= W ? NT / W : 1;   // row tiles per wave
+  static constexpr int PT = NT >= W ? 4 : 4 * NT / W;  // p-tiles per wave
   static __device__ __forceinline__ int tile(int k, int w) {
+    if (NT < W) return w % NT;                // NT = 4, W = 8
+    if (W == 4) {                             // tiles w, 7-w, 8+w, 15-w
+      const int pi = k >> 1;
+      return (k & 1) ? 8 * pi + 7 - w : 8 * pi + w;
+    }
+    // W = 8: SIMD s = w%4 owns tiles s, 7-s (NT = 8) or s, 7-s, 8+s, 15-s
+    // (NT = 16), shared by its two waves
     const int s = w & 3, hf = w >> 2;
-    if (NT == 4) return s;
     if (NT == 8) return hf ? 7 - s : s;
     return hf ? (k ? 8 + s : 7 - s) : (k ? 15 - s : s);
   }
-  static __device__ __forceinline__ int pt0(int w) { return NT == 4 ? 2 * (w >> 2) : 0; }
+  static __device__ __forceinline__ int pt0(int w) { return NT < W ? PT * (w / NT) : 0; }
 };
 
 __device__ __forceinline__ int nblocks(int Qc) { return (Qc + kJB - 1) / kJB; }
@@ -483,12 +517,14 @@ __device__ __forceinline__ int nblocks(int Qc) { return (Qc + kJB - 1) / kJB; }
 // state each of the first ngroups-1 groups builds from a zero start, and the
 // group's total decay.  Blocks of B and x are prefetched one ahead.
 template <int Q, int N, bool F32, class IO>
-__global__ __launch_bounds__(kThreads, F32 ? 2 : 4) void ssd_group_state_kernel(Params p) {
-  using T = typename Mma<F32>::T;
+__global__ __launch_bounds__(512, F32 ? 2 : 4) void ssd_group_state_kernel(Params p) {
+  constexpr int W = 8, T = 64 * W;
+  using E = typename Mma<F32>::T;
+  using SS = StateSplit<N, W>;
   constexpr int LDJ = kJB + 8;
-  constexpr int NN = N / 32;
-  __shared__ __attribute__((aligned(16))) T sBT[N * LDJ];
-  __shared__ __attribute__((aligned(16))) T sXT[kP * LDJ];
+  constexpr int NN = SS::NN;
+  __shared__ __attribute__((aligned(16))) E sBT[N * LDJ];
+  __shared__ __attribute__((aligned(16))) E sXT[kP * LDJ];
   __shared__ __attribute__((aligned(16))) ChunkLds<Q> clb[2];
 
   int64_t b, h, j;
@@ -504,9 +540,9 @@ __global__ __launch_bounds__(kThreads, F32 ? 2 : 4) void ssd_group_state_kernel(
   const int64_t c_begin = j * p.cpg, c_end = c_begin + p.cpg;  // never the last group
   auto qc_of = [&](int64_t c) { return (int)((p.L - c * Q) < Q ? (p.L - c * Q) : Q); };
 
-  BlockRaw<N, IO> nxt;
-  load_block<N, IO>(sv, (uint32_t)(c_begin * Q), 0, nxt);
-  float2 ldv = load_lamd<Q>(p, bh, c_begin);
+  BlockRaw<N, IO, T> nxt;
+  load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), 0, nxt);
+  float2 ldv = load_lamd<Q, T>(p, bh, c_begin);
   float2 civ = p.cinfo[bh * p.nc + c_begin];
   for (int64_t c = c_begin; c < c_end; ++c) {
     const uint32_t t0 = (uint32_t)(c * Q);
@@ -515,7 +551,7 @@ __global__ __launch_bounds__(kThreads, F32 ? 2 : 4) void ssd_group_state_kernel(
     const float lend2 = civ.x;
     chunk_prep<Q>(ldv, lend2, cl);
     if (c + 1 < c_end) {
-      ldv = load_lamd<Q>(p, bh, c + 1);
+      ldv = load_lamd<Q, T>(p, bh, c + 1);
       civ = p.cinfo[bh * p.nc + c + 1];
     }
     const float dec = fast_exp2(lend2);
@@ -525,13 +561,13 @@ __global__ __launch_bounds__(kThreads, F32 ? 2 : 4) void ssd_group_state_kernel(
     const int nb = nblocks(Qc);
     for (int jb = 0; jb < nb; ++jb) {
       lds_barrier();
-      store_block<N, F32, IO, false>(nxt, jb, cl.w, nullptr, sBT, sXT);
+      store_block<N, F32, IO, T, false>(nxt, jb, cl.w, nullptr, sBT, sXT);
       lds_barrier();
       if (jb + 1 < nb)
-        load_block<N, IO>(sv, t0, jb + 1, nxt);
+        load_block<N, IO, T>(sv, t0, jb + 1, nxt);
       else if (c + 1 < c_end)
-        load_block<N, IO>(sv, t0 + Q, 0, nxt);
-      state_block_mma<N, F32>(sXT, sBT, sacc);
+        load_block<N, IO, T>(sv, t0 + Q, 0, nxt);
+      state_block_mma<N, F32, W>(sXT, sBT, sacc);
     }
   }
   const int64_t slot = bh * (p.ngroups - 1) + j;
@@ -539,7 +575,7 @@ __global__ __launch_bounds__(kThreads, F32 ? 2 : 4) void ssd_group_state_kernel(
 #pragma unroll
   for (int t = 0; t < NN; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[state_row(r) * N + state_col<N>(t)] = sacc[t][r];
+    for (int r = 0; r < 4; ++r) dst[SS::row(r) * N + SS::col(t)] = sacc[t][r];
   if (threadIdx.x == 0) p.grp_lam[slot] = lgrp;
 }
 
@@ -559,28 +595,29 @@ __global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p, int PN
   }
 }
 
-// Main pass: chunk_scan over the chunks of one group, carrying the state.
-// Per chunk: discretise + cumsum, inter-chunk term C.S_in^T from the carried
-// state, then per 64-token block the intra-chunk term and the block's
-// contribution to the carried state; the next block's loads are issued
-// before the current block's matrix work.
-template <int Q, int N, bool F32, class IO>
-__global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
-  using T = typename Mma<F32>::T;
+// Main pass: chunk_scan over the chunks of one group with W waves, carrying
+// the state.  Per chunk: the inter-chunk term C.S_in^T from the carried
+// state, then per 64-token block the intra-chunk term, the block's
+// contribution to the carried state and the epilogue of the rows the block
+// completes; the next block's loads are issued before its matrix work.
+template <int Q, int N, bool F32, class IO, int W, bool HAS_Z>
+__global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
+  constexpr int T = 64 * W;
+  using E = typename Mma<F32>::T;
   using frag = typename Mma<F32>::frag;
   using quad = typename Mma<F32>::quad;
-  using RS = RowSplit<Q>;
+  using RS = RowSplit<Q, W>;
+  using SS = StateSplit<N, W>;
   constexpr int NR = RS::NR, PT = RS::PT;
   constexpr int KB = N / 32;  // K blocks over the state dim
-  constexpr int NN = N / 32;  // state n-tiles per wave
-  constexpr int LDN = N + 8, LDJ = kJB + 8;
-  __shared__ __attribute__((aligned(16))) T sB[kJB * LDN];
-  __shared__ __attribute__((aligned(16))) T sBT[N * LDJ];
-  __shared__ __attribute__((aligned(16))) T sXT[kP * LDJ];
-  __shared__ __attribute__((aligned(16))) T sS[kP * LDN];
-  __shared__ __attribute__((aligned(16))) float sZ[kJB * (kP + 4)];
+  constexpr int NN = SS::NN;
+  constexpr int LDN = N + 8, LDJ = kJB + 8, LDZ = kP + 4;
+  __shared__ __attribute__((aligned(16))) E sB[kJB * LDN];
+  __shared__ __attribute__((aligned(16))) E sBT[N * LDJ];
+  __shared__ __attribute__((aligned(16))) E sXT[kP * LDJ];
+  __shared__ __attribute__((aligned(16))) E sS[kP * LDN];
+  __shared__ __attribute__((aligned(16))) float sZ[HAS_Z ? kJB * LDZ : 4];
   __shared__ __attribute__((aligned(16))) ChunkLds<Q> clb[2];
-  constexpr int LDZ = kP + 4;
 
   int64_t b, h, j;
   if (!decode_tile(p, p.ngroups, b, h, j)) return;
@@ -591,8 +628,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
   const uint64_t lhp = (uint64_t)p.L * p.H * kP;
   const int osz = p.out_bf16 ? 2 : 4, zsz = p.z_bf16 ? 2 : 4;
   const rsrc_t rout = make_rsrc(static_cast<char *>(p.out) + b * lhp * osz, (uint32_t)(lhp * osz));
-  const rsrc_t rz = make_rsrc(p.z ? static_cast<const char *>(p.z) + b * lhp * zsz : nullptr,
-                              p.z ? (uint32_t)(lhp * zsz) : 0u);
+  const rsrc_t rz = make_rsrc(HAS_Z ? static_cast<const char *>(p.z) + b * lhp * zsz : nullptr,
+                              HAS_Z ? (uint32_t)(lhp * zsz) : 0u);
+  const bool z_bf16 = p.z_bf16 != 0;
   const float Dh = p.D ? p.D[h] : 0.f;
   const int64_t bh = b * p.H + h;
   const int64_t c_begin = j * p.cpg;
@@ -601,15 +639,14 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
 
   // prefetch registers: next 64-token block (and its z), next chunk's C rows
   // and records
-  const bool has_z = p.z != nullptr, z_bf16 = p.z_bf16 != 0;
-  BlockRaw<N, IO> nxt;
-  ZRaw nz;
+  BlockRaw<N, IO, T> nxt;
+  ZRaw<T> nz;
   auto load_zb = [&](uint32_t t0, int jb) {
-    if (has_z) load_z(rz, z_bf16, sv.H, sv.h, t0, jb, nz);
+    if (HAS_Z) load_z<T>(rz, z_bf16, sv.H, sv.h, t0, jb, nz);
   };
-  load_block<N, IO>(sv, (uint32_t)(c_begin * Q), 0, nxt);
+  load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), 0, nxt);
   load_zb((uint32_t)(c_begin * Q), 0);
-  float2 ldv = load_lamd<Q>(p, bh, c_begin);
+  float2 ldv = load_lamd<Q, T>(p, bh, c_begin);
   float2 civ = p.cinfo[bh * p.nc + c_begin];
   typename IO::raw8 craw[NR][KB];
   auto load_c = [&](uint32_t t0) {
@@ -625,7 +662,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
   if (kPrefetchC) load_c((uint32_t)(c_begin * Q));
 
   // state entering this group: h0 / zero for the first, the chained group
-  // state otherwise, in accumulator layout (see state_block_mma)
+  // state otherwise
   f32x4 sacc[NN];
   {
     const float *init = (j == 0) ? (p.h0 ? p.h0 + bh * (int64_t)(kP * N) : nullptr)
@@ -634,9 +671,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
     for (int t = 0; t < NN; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = state_row(r), col = state_col<N>(t);
+        const int row = SS::row(r), col = SS::col(t);
         sacc[t][r] = init ? init[row * N + col] : 0.f;
-        sS[row * LDN + col] = (T)sacc[t][r];
+        sS[row * LDN + col] = (E)sacc[t][r];
       }
   }
 
@@ -650,7 +687,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
     chunk_prep<Q>(ldv, lend2, cl);
     lds_barrier();
     if (c + 1 < c_end) {
-      ldv = load_lamd<Q>(p, bh, c + 1);
+      ldv = load_lamd<Q, T>(p, bh, c + 1);
       civ = p.cinfo[bh * p.nc + c + 1];
     }
 
@@ -661,7 +698,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int s = 0; s < 8; ++s) cfr[k][kb][s] = (T)IO::cvt8(craw[k][kb], s);
+        for (int s = 0; s < 8; ++s) cfr[k][kb][s] = (E)IO::cvt8(craw[k][kb], s);
 
     // inter-chunk term: Y = diag(exp(Lam)) C S_in^T
     f32x4 yacc[NR][PT];
@@ -694,14 +731,14 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
     const int nb = nblocks(Qc);
     for (int jb = 0; jb < nb; ++jb) {
       lds_barrier();
-      store_block<N, F32, IO, true>(nxt, jb, cl.w, sB, sBT, sXT);
-      if (has_z) store_z(nz, z_bf16, sZ);
+      store_block<N, F32, IO, T, true>(nxt, jb, cl.w, sB, sBT, sXT);
+      if (HAS_Z) store_z<T>(nz, z_bf16, sZ);
       lds_barrier();
       if (jb + 1 < nb) {
-        load_block<N, IO>(sv, t0, jb + 1, nxt);
+        load_block<N, IO, T>(sv, t0, jb + 1, nxt);
         load_zb(t0, jb + 1);
       } else if (c + 1 < c_end) {
-        load_block<N, IO>(sv, t0 + Q, 0, nxt);
+        load_block<N, IO, T>(sv, t0 + Q, 0, nxt);
         load_zb(t0 + Q, 0);
         if (kPrefetchC) load_c(t0 + Q);
       }
@@ -765,19 +802,19 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
           if (jbase + 31 > row0) {  // the sub-block meets the diagonal: mask j > i
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              mf[r] = (T)(ja0 + r <= i ? ma[r] : 0.f);
-              mf[4 + r] = (T)(ja0 + 16 + r <= i ? mc[r] : 0.f);
+              mf[r] = (E)(ja0 + r <= i ? ma[r] : 0.f);
+              mf[4 + r] = (E)(ja0 + 16 + r <= i ? mc[r] : 0.f);
             }
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              mf[r] = (T)ma[r];
-              mf[4 + r] = (T)mc[r];
+              mf[r] = (E)ma[r];
+              mf[4 + r] = (E)mc[r];
             }
           }
 #pragma unroll
           for (int pt = 0; pt < PT; ++pt) {
-            const T *xrow = &sXT[(16 * (pt0 + pt) + lr) * LDJ + 32 * js + 4 * lq];
+            const E *xrow = &sXT[(16 * (pt0 + pt) + lr) * LDJ + 32 * js + 4 * lq];
             const quad lo = *reinterpret_cast<const quad *>(xrow);
             const quad hi = *reinterpret_cast<const quad *>(xrow + 16);
             frag xb;
@@ -790,8 +827,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
           }
         }
       }
+
       // chunk_state contribution of this block to the carried state
-      state_block_mma<N, F32>(sXT, sBT, sacc);
+      state_block_mma<N, F32, W>(sXT, sBT, sacc);
 
       // epilogue of the row tiles that lie in this block (their sums are
       // complete): + D x with x from the staged block, the z gate from the
@@ -809,7 +847,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float y = yacc[k][pt][r] + Dh * (float)xq[r];
-            if (has_z) {
+            if (HAS_Z) {
               const float zz = sZ[(lrow + r) * LDZ + col];
               y *= zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz));
             }
@@ -828,8 +866,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
 #pragma unroll
     for (int t = 0; t < NN; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sS[state_row(r) * LDN + state_col<N>(t)] = (T)sacc[t][r];
+      for (int r = 0; r < 4; ++r) sS[SS::row(r) * LDN + SS::col(t)] = (E)sacc[t][r];
   }
 
   if (p.ret_final && j == p.ngroups - 1) {
@@ -837,7 +874,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(Params p) {
 #pragma unroll
     for (int t = 0; t < NN; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[state_row(r) * N + state_col<N>(t)] = sacc[t][r];
+      for (int r = 0; r < 4; ++r) dst[SS::row(r) * N + SS::col(t)] = sacc[t][r];
   }
 }
 
@@ -928,7 +965,7 @@ ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, con
   if (pl.ngroups > 1) {
     const int64_t t1 = bh * (pl.ngroups - 1);
     const int64_t g1 = 8 * ((t1 + 7) / 8);
-    hipLaunchKernelGGL((ssd_group_state_kernel<Q, N, F32, IO>), dim3((unsigned)g1), dim3(kThreads),
+    hipLaunchKernelGGL((ssd_group_state_kernel<Q, N, F32, IO>), dim3((unsigned)g1), dim3(512),
                        0, stream, prm);
     const int PN = kP * N;
     hipLaunchKernelGGL(ssd_group_passing_kernel, dim3((unsigned)(bh * (PN / 256))), dim3(256), 0,
@@ -938,8 +975,15 @@ ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, con
   const int64_t g2 = 8 * ((t2 + 7) / 8);
   if (d->ev_main_begin && hipEventRecord(static_cast<hipEvent_t>(d->ev_main_begin), stream) != hipSuccess)
     return SSD_ERR_LAUNCH;
-  hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, F32, IO>), dim3((unsigned)g2), dim3(kThreads), 0,
-                     stream, prm);
+  // 4-wave workgroups (two per CU) for chunks of 64 and 128 tokens; 8 waves
+  // for 256-token chunks, whose row tiles would not fit 4 waves' registers
+  constexpr int W = Q == 256 ? 8 : 4;
+  if (prm.z)
+    hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, F32, IO, W, true>), dim3((unsigned)g2),
+                       dim3(64 * W), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, F32, IO, W, false>), dim3((unsigned)g2),
+                       dim3(64 * W), 0, stream, prm);
   if (hipGetLastError() != hipSuccess) return SSD_ERR_LAUNCH;
   if (d->ev_main_end && hipEventRecord(static_cast<hipEvent_t>(d->ev_main_end), stream) != hipSuccess)
     return SSD_ERR_LAUNCH;
