@@ -926,20 +926,23 @@ ssd_status check_shape(const ssd_desc *d, int64_t chunk) {
   return SSD_OK;
 }
 
-// Workgroups the plan aims for: two per CU on a 256-CU MI355X.
-constexpr int64_t kTargetWorkgroups = 512;
+// Workgroups the plan aims for on a 256-CU MI355X: one per CU for 8-wave
+// workgroups (256-token chunks), two per CU for 4-wave ones.  A sequence is
+// cut into chunk groups only when (b, h) pairs alone fall short of that.
+int64_t target_workgroups(int64_t chunk) { return chunk == 256 ? 256 : 512; }
 
 Plan make_plan(const ssd_desc *d, int64_t chunk) {
   Plan pl;
   pl.nc = (d->seqlen + chunk - 1) / chunk;
   const int64_t bh = d->batch * d->nheads;
+  const int64_t target = target_workgroups(chunk);
   int64_t cpg;
   if (d->chunks_per_wg > 0) {
     cpg = d->chunks_per_wg;
-  } else if (bh >= kTargetWorkgroups) {
+  } else if (bh >= target) {
     cpg = pl.nc;
   } else {
-    const int64_t want = (kTargetWorkgroups + bh - 1) / bh;
+    const int64_t want = (2 * 256 + bh - 1) / bh;  // groups per (b, h)
     cpg = pl.nc / want;
   }
   if (cpg < 1) cpg = 1;
