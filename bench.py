@@ -56,6 +56,27 @@ def algorithmic_flops(w: Workload) -> int:
     return 2 * w.batch * nc * (G * Q * Q * N + H * Q * Q * P + 2 * H * Q * N * P)
 
 
+def measured_traffic(w: Workload):
+    """HBM bytes per main-kernel launch measured with rocprofv3 counters
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated; profiles/traffic.json), or
+    None when the kernel source changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(here, rec.get("kernel_source", ""))
+    if not os.path.exists(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec.get("kernel_source_sha256"):
+            return None
+    k = rec.get("workloads", {}).get(w.name, {}).get("ssd_chunk_scan_kernel")
+    return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
+
+
 class HipEvents:
     """Raw HIP events via the HIP runtime (recorded inside the library)."""
 
@@ -246,7 +267,7 @@ def main(argv=None):
                    "initial_state": w.has_h0, "final_state": True,
                    "chunks_per_wg": cpg, "chunk_groups": ngroups, "input_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w),
                      "kernel": "ssd_chunk_scan_kernel", "kernel_ms": main_mean,
                      "algorithmic_bytes": abytes},
         "path": {"ms": ms_per_step, "gbs": abytes / (wall / K) / 1e9,
