@@ -274,11 +274,13 @@ template <int Q> struct ChunkLds {
   float lam[Q], delta[Q], w[Q], u[Q], mid[Q / 32];
 };
 
-// This thread's {Lam, delta} record of a chunk (threads past Q load nothing).
+// This thread's {Lam, delta} record of a chunk.  Threads past Q re-read
+// record Q-1 (and ignore it): every prefetch here is unconditional, because a
+// load under a branch makes the compiler merge the old and new registers
+// after the load returns, which waits for all loads in flight.
 template <int Q, int T>
 __device__ __forceinline__ float2 load_lamd(const Params &p, int64_t bh, int64_t c) {
-  const int tid = threadIdx.x;
-  if (Q < T && tid >= Q) return make_float2(0.f, 0.f);
+  const int tid = (Q < T && (int)threadIdx.x >= Q) ? Q - 1 : (int)threadIdx.x;
   return p.lamd[(bh * p.nc + c) * Q + tid];
 }
 
@@ -313,31 +315,50 @@ struct BlockRaw {
   typename IO::raw4 x[KX][4];
 };
 
-// Issue the loads of block jb of the chunk starting at t0.
+// Staging unit u -> (token quad rg in 0..15, column quad cg).  Every 64
+// consecutive units cover an 8 x 8 tile of (rg, cg) pairs, so one wave's load
+// of a row reads 8 column quads (a whole 128-byte line of fp32).  Inside each
+// 16-unit group the pairs lie on a diagonal band: both the row-major writes
+// (rows 4rg+e, 8-byte column quads) and the transposed writes (rows 4cg+c,
+// 8-byte token quads) of the group then fall on 16 distinct LDS bank pairs
+// (LDS writes serve 16 lanes of 8 bytes per cycle over 32 banks).
+__device__ __forceinline__ void unit_of(int u, int &rg, int &cg) {
+  const int i = u & 15, d = (u >> 4) & 3, t = u >> 6, q = i >> 2;
+  rg = (i & 1) + 2 * q + 8 * (t & 1);
+  cg = ((i >> 1) & 1) + 2 * ((q + d) & 3) + 8 * (t >> 1);
+}
+
+// Past-the-end element offset: the buffer range check turns a load from it
+// into zeros (no memory access).  Every row buffer is below 2^31 bytes.
+constexpr uint32_t kNoElem = 0x20000000u;
+
+// Issue the loads of the 64-token block starting at token tb.  The loads are
+// unconditional (units past the block's count read kNoElem) so that they stay
+// in flight until the block is stored.
 template <int N, class IO, int T>
-__device__ __forceinline__ void load_block(const SeqView<N, IO> &sv, uint32_t t0, int jb,
+__device__ __forceinline__ void load_block(const SeqView<N, IO> &sv, uint32_t tb,
                                            BlockRaw<N, IO, T> &r) {
   using BR = BlockRaw<N, IO, T>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < BR::KB_; ++k) {
     const int u = tid + T * k;
-    if (u < BR::UB) {
-      const int ng = u % BR::NG, rg = u / BR::NG;
+    const bool ok = BR::UB % T == 0 || u < BR::UB;
+    int rg, ng;
+    unit_of(u, rg, ng);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        r.b[k][e] = IO::load4(sv.B, sv.boff(t0 + kJB * jb + 4 * rg + e, 4 * ng));
-    }
+    for (int e = 0; e < 4; ++e)
+      r.b[k][e] = IO::load4(sv.B, ok ? sv.boff(tb + 4 * rg + e, 4 * ng) : kNoElem);
   }
 #pragma unroll
   for (int k = 0; k < BR::KX; ++k) {
     const int u = tid + T * k;
-    if (u < BR::UX) {
-      const int pg = u % (kP / 4), rg = u / (kP / 4);
+    const bool ok = BR::UX % T == 0 || u < BR::UX;
+    int rg, pg;
+    unit_of(u, rg, pg);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        r.x[k][e] = IO::load4(sv.x, sv.xoff(t0 + kJB * jb + 4 * rg + e, 4 * pg));
-    }
+    for (int e = 0; e < 4; ++e)
+      r.x[k][e] = IO::load4(sv.x, ok ? sv.xoff(tb + 4 * rg + e, 4 * pg) : kNoElem);
   }
 }
 
@@ -358,7 +379,8 @@ __device__ __forceinline__ void store_block(const BlockRaw<N, IO, T> &r, int jb,
   for (int k = 0; k < BR::KB_; ++k) {
     const int u = tid + T * k;
     if (u < BR::UB) {
-      const int ng = u % BR::NG, rg = u / BR::NG;
+      int rg, ng;
+      unit_of(u, rg, ng);
       const int r0 = 4 * rg;
       const f32x4 wgt = *reinterpret_cast<const f32x4 *>(&sw[kJB * jb + r0]);
       f32x4 v[4];
@@ -385,7 +407,8 @@ __device__ __forceinline__ void store_block(const BlockRaw<N, IO, T> &r, int jb,
   for (int k = 0; k < BR::KX; ++k) {
     const int u = tid + T * k;
     if (u < BR::UX) {
-      const int pg = u % (kP / 4), rg = u / (kP / 4);
+      int rg, pg;
+      unit_of(u, rg, pg);
       const int r0 = 4 * rg;
       f32x4 v[4];
 #pragma unroll
@@ -411,12 +434,12 @@ struct ZRaw {
 };
 
 template <int T>
-__device__ __forceinline__ void load_z(rsrc_t rz, bool bf16, uint32_t H, uint32_t h, uint32_t t0,
-                                       int jb, ZRaw<T> &r) {
+__device__ __forceinline__ void load_z(rsrc_t rz, bool bf16, uint32_t H, uint32_t h, uint32_t tb,
+                                       ZRaw<T> &r) {
 #pragma unroll
   for (int k = 0; k < ZRaw<T>::K; ++k) {
     const int u = threadIdx.x + T * k;
-    const uint32_t off = ((t0 + kJB * jb + u / 8) * H + h) * kP + 8 * (u % 8);
+    const uint32_t off = ((tb + u / 8) * H + h) * kP + 8 * (u % 8);
     if (bf16) {
       r.lo[k] = IoBF16::load8(rz, off);
     } else {
@@ -443,9 +466,12 @@ __device__ __forceinline__ void store_z(const ZRaw<T> &r, bool bf16, float *sZ) 
       lo = __builtin_bit_cast(f32x4, r.lo[k]);
       hi = __builtin_bit_cast(f32x4, r.hi[k]);
     }
+    // lanes 4..7 of each group of 8 write their halves in the other order,
+    // so each 16-byte write instruction covers all 32 banks once
     float *dst = &sZ[(u / 8) * LDZ + 8 * (u % 8)];
-    *reinterpret_cast<f32x4 *>(dst) = lo;
-    *reinterpret_cast<f32x4 *>(dst + 4) = hi;
+    const bool sw = (u & 4) != 0;
+    *reinterpret_cast<f32x4 *>(dst + (sw ? 4 : 0)) = sw ? hi : lo;
+    *reinterpret_cast<f32x4 *>(dst + (sw ? 0 : 4)) = sw ? lo : hi;
   }
 }
 
@@ -541,7 +567,7 @@ __global__ __launch_bounds__(512, F32 ? 2 : 4) void ssd_group_state_kernel(Param
   auto qc_of = [&](int64_t c) { return (int)((p.L - c * Q) < Q ? (p.L - c * Q) : Q); };
 
   BlockRaw<N, IO, T> nxt;
-  load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), 0, nxt);
+  load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), nxt);
   float2 ldv = load_lamd<Q, T>(p, bh, c_begin);
   float2 civ = p.cinfo[bh * p.nc + c_begin];
   for (int64_t c = c_begin; c < c_end; ++c) {
@@ -550,9 +576,10 @@ __global__ __launch_bounds__(512, F32 ? 2 : 4) void ssd_group_state_kernel(Param
     ChunkLds<Q> &cl = clb[c & 1];
     const float lend2 = civ.x;
     chunk_prep<Q>(ldv, lend2, cl);
-    if (c + 1 < c_end) {
-      ldv = load_lamd<Q, T>(p, bh, c + 1);
-      civ = p.cinfo[bh * p.nc + c + 1];
+    {
+      const int64_t cn = (c + 1 < c_end) ? c + 1 : c;
+      ldv = load_lamd<Q, T>(p, bh, cn);
+      civ = p.cinfo[bh * p.nc + cn];
     }
     const float dec = fast_exp2(lend2);
 #pragma unroll
@@ -563,10 +590,11 @@ __global__ __launch_bounds__(512, F32 ? 2 : 4) void ssd_group_state_kernel(Param
       lds_barrier();
       store_block<N, F32, IO, T, false>(nxt, jb, cl.w, nullptr, sBT, sXT);
       lds_barrier();
-      if (jb + 1 < nb)
-        load_block<N, IO, T>(sv, t0, jb + 1, nxt);
-      else if (c + 1 < c_end)
-        load_block<N, IO, T>(sv, t0 + Q, 0, nxt);
+      // next block: the chunk's next one, else the next chunk's first, else
+      // (last block of the group) this one again, unused
+      const uint32_t tn = (jb + 1 < nb) ? t0 + kJB * (jb + 1)
+                                        : (c + 1 < c_end) ? t0 + Q : t0 + kJB * jb;
+      load_block<N, IO, T>(sv, tn, nxt);
       state_block_mma<N, F32, W>(sXT, sBT, sacc);
     }
   }
@@ -641,11 +669,11 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   // and records
   BlockRaw<N, IO, T> nxt;
   ZRaw<T> nz;
-  auto load_zb = [&](uint32_t t0, int jb) {
-    if (HAS_Z) load_z<T>(rz, z_bf16, sv.H, sv.h, t0, jb, nz);
+  auto load_zb = [&](uint32_t tb) {
+    if (HAS_Z) load_z<T>(rz, z_bf16, sv.H, sv.h, tb, nz);
   };
-  load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), 0, nxt);
-  load_zb((uint32_t)(c_begin * Q), 0);
+  load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), nxt);
+  load_zb((uint32_t)(c_begin * Q));
   float2 ldv = load_lamd<Q, T>(p, bh, c_begin);
   float2 civ = p.cinfo[bh * p.nc + c_begin];
   typename IO::raw8 craw[NR][KB];
@@ -663,18 +691,23 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
 
   // state entering this group: h0 / zero for the first, the chained group
   // state otherwise
+  // (all loads issued before any is used; a null start reads as zeros
+  // through an empty buffer range)
   f32x4 sacc[NN];
   {
     const float *init = (j == 0) ? (p.h0 ? p.h0 + bh * (int64_t)(kP * N) : nullptr)
                                  : p.grp_state + (bh * (p.ngroups - 1) + (j - 1)) * (int64_t)(kP * N);
+    const rsrc_t ri = make_rsrc(init, init ? (uint32_t)(kP * N * 4) : 0u);
 #pragma unroll
     for (int t = 0; t < NN; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = SS::row(r), col = SS::col(t);
-        sacc[t][r] = init ? init[row * N + col] : 0.f;
-        sS[row * LDN + col] = (E)sacc[t][r];
-      }
+      for (int r = 0; r < 4; ++r)
+        sacc[t][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            ri, (uint32_t)(SS::row(r) * N + SS::col(t)) * 4, 0, 0));
+#pragma unroll
+    for (int t = 0; t < NN; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sS[SS::row(r) * LDN + SS::col(t)] = (E)sacc[t][r];
   }
 
   for (int64_t c = c_begin; c < c_end; ++c) {
@@ -686,9 +719,10 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
     const bool factored = civ.y != 0.f;
     chunk_prep<Q>(ldv, lend2, cl);
     lds_barrier();
-    if (c + 1 < c_end) {
-      ldv = load_lamd<Q, T>(p, bh, c + 1);
-      civ = p.cinfo[bh * p.nc + c + 1];
+    {
+      const int64_t cn = (c + 1 < c_end) ? c + 1 : c;
+      ldv = load_lamd<Q, T>(p, bh, cn);
+      civ = p.cinfo[bh * p.nc + cn];
     }
 
     // B operand of B.C^T and A operand of C.S^T share this layout
@@ -734,13 +768,14 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
       store_block<N, F32, IO, T, true>(nxt, jb, cl.w, sB, sBT, sXT);
       if (HAS_Z) store_z<T>(nz, z_bf16, sZ);
       lds_barrier();
-      if (jb + 1 < nb) {
-        load_block<N, IO, T>(sv, t0, jb + 1, nxt);
-        load_zb(t0, jb + 1);
-      } else if (c + 1 < c_end) {
-        load_block<N, IO, T>(sv, t0 + Q, 0, nxt);
-        load_zb(t0 + Q, 0);
-        if (kPrefetchC) load_c(t0 + Q);
+      {
+        // next block: the chunk's next one, else the next chunk's first, else
+        // (last block of the group) this one again, unused
+        const bool last = jb + 1 == nb;
+        const uint32_t tn = !last ? t0 + kJB * (jb + 1) : (c + 1 < c_end) ? t0 + Q : t0 + kJB * jb;
+        load_block<N, IO, T>(sv, tn, nxt);
+        load_zb(tn);
+        if (kPrefetchC && last) load_c((c + 1 < c_end) ? t0 + Q : t0);
       }
       // intra-chunk term for this wave's row tiles against tokens of block jb,
       // one 32-token sub-block at a time (its B fragments serve every row
@@ -840,6 +875,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
         const int row0 = 16 * RS::tile(k, w);
         if ((row0 >> 6) != jb) continue;
         const int lrow = row0 - kJB * jb + 4 * lq;  // row within the block, + r
+        f32x4 yv[PT];
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
           const int col = 16 * (pt0 + pt) + lr;
@@ -851,12 +887,25 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
               const float zz = sZ[(lrow + r) * LDZ + col];
               y *= zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz));
             }
-            const uint32_t off = sv.xoff(t0 + kJB * jb + lrow + r, col);
-            if (p.out_bf16)
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(y), rout, off * 2, 0, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rout, off * 4, 0, 0);
+            yv[pt][r] = y;
           }
+        }
+        const uint32_t off0 = sv.xoff(t0 + kJB * jb + lrow, 16 * pt0 + lr);
+        const uint32_t rstep = sv.H * kP;  // elements between consecutive tokens
+        if (p.out_bf16) {
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(yv[pt][r]), rout,
+                                                    (off0 + r * rstep + 16 * pt) * 2, 0, 0);
+        } else {
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[pt][r]), rout,
+                                                    (off0 + r * rstep + 16 * pt) * 4, 0, 0);
         }
       }
     }
