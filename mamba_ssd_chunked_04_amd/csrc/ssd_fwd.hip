@@ -33,6 +33,7 @@
 #include <stdint.h>
 #include <string.h>
 
+
 #include "../../include/ssd_mi355x.h"
 
 namespace {
@@ -162,8 +163,6 @@ struct Params {
   const float *h0;
   void *out;
   float *final_state;
-  float2 *lamd;      // [B*H][nc][Q]: per token {Lam (log2, inclusive in-chunk), delta}
-  float2 *cinfo;     // [B*H][nc]: per chunk {Lam_end, 1 if the factored decay is safe}
   float *grp_state;  // [B*H][ngroups-1][P*N]: group aggregates, then entering states
   float *grp_lam;    // [B*H][ngroups-1]: group total log2-decay
   int64_t batch, L, H, G, nc, ngroups, cpg;
@@ -220,85 +219,102 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// chunk_cumsum (its own kernel, ahead of the matrix passes): for one
-// (b, h, chunk), discretise dt (dt_bias, softplus, clamp), then the inclusive
-// in-chunk prefix Lam of delta*A in log2 units.  Tokens past the sequence end
-// get delta = 0, so they decay nothing and add nothing.  Writes {Lam, delta}
-// per token and {Lam_end, factored} per chunk, where factored says whether
-// |delta*A| <= 7 (log2 units) for every token of the chunk, which keeps the
-// factored intra-chunk decay of the main pass inside fp32 range.
-template <int Q>
-__global__ __launch_bounds__(256) void ssd_chunk_cumsum_kernel(Params p) {
-  __shared__ float wave_sum[4];
-  __shared__ int wave_big[4];
-  const int64_t bhc = blockIdx.x;
-  const int64_t c = bhc % p.nc, bh = bhc / p.nc;
-  const int64_t b = bh / p.H, h = bh % p.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t = c * Q + tid;
-  float a = 0.f, delta = 0.f;
-  if (t < p.L) {
-    float u = p.dt[(b * p.L + t) * p.H + h] + (p.dt_bias ? p.dt_bias[h] : 0.f);
-    if (p.dt_softplus) u = (u > 20.f) ? u : __logf(1.f + __expf(u));
-    delta = fminf(fmaxf(u, p.dt_min), p.dt_max);
-    a = delta * p.A[h] * kLog2e;
-  }
-  float v = a;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float nb = __shfl_up(v, off, 64);
-    if (lane >= off) v += nb;
-  }
-  const uint64_t big = __ballot(fabsf(a) > 7.f);
-  if (lane == 63) wave_sum[wave] = v;
-  if (lane == 0) wave_big[wave] = big != 0;
-  __syncthreads();
-  float pre = 0.f, tot = 0.f;
-  int bigc = 0;
-#pragma unroll
-  for (int w = 0; w < Q / 64; ++w) {
-    tot += wave_sum[w];
-    pre += (w < wave) ? wave_sum[w] : 0.f;
-    bigc |= wave_big[w];
-  }
-  p.lamd[bhc * Q + tid] = make_float2(v + pre, delta);
-  if (tid == 0) p.cinfo[bhc] = make_float2(tot, bigc ? 0.f : 1.f);
-}
-
 // Per-chunk scalars in LDS (Lam in log2 units).
 //   lam[j]   inclusive in-chunk prefix of delta*A;  delta[j]
 //   w[j]     exp(Lam_end - Lam_j) delta_j      (chunk_state weights)
 //   u[j]     exp(Lam_m - Lam_j) delta_j, m the reference token (16th) of j's
 //            32-token sub-block; mid[j/32] = Lam_m
+//   dts[j]   raw dt of token j, staged one chunk ahead
 template <int Q> struct ChunkLds {
-  float lam[Q], delta[Q], w[Q], u[Q], mid[Q / 32];
+  float lam[Q], delta[Q], w[Q], u[Q], dts[Q], mid[Q / 32];
 };
 
-// This thread's {Lam, delta} record of a chunk.  Threads past Q re-read
-// record Q-1 (and ignore it): every prefetch here is unconditional, because a
-// load under a branch makes the compiler merge the old and new registers
-// after the load returns, which waits for all loads in flight.
-template <int Q, int T>
-__device__ __forceinline__ float2 load_lamd(const Params &p, int64_t bh, int64_t c) {
-  const int tid = (Q < T && (int)threadIdx.x >= Q) ? Q - 1 : (int)threadIdx.x;
-  return p.lamd[(bh * p.nc + c) * Q + tid];
+// chunk_cumsum inside the matrix passes.  The raw dt of a chunk is loaded
+// two chunks ahead, one token per thread, and staged in the chunk's LDS
+// scalars one chunk ahead.  Lane l of every wave then takes the tokens
+// l + 64 m of the chunk (m < Q/64) and computes, redundantly in each wave,
+// delta = clamp(softplus(dt + dt_bias)) (0 past the sequence end) and the
+// inclusive in-chunk prefix Lam of delta*A in log2 units (a wavefront scan
+// per 64 tokens plus the running total of the earlier ones).
+// Threads past Q re-load token Q-1 (unused): the load stays unconditional.
+__device__ __forceinline__ float load_dt(rsrc_t rdt, uint32_t H, uint32_t h, uint32_t t0, int Q) {
+  const uint32_t i = threadIdx.x < (uint32_t)Q ? threadIdx.x : (uint32_t)Q - 1;
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, ((t0 + i) * H + h) * 4, 0, 0));
 }
 
-// Fill the chunk's LDS scalars from the prefetched records (caller puts a
-// barrier before any reader).
 template <int Q>
-__device__ __forceinline__ void chunk_prep(float2 ld, float lend2, ChunkLds<Q> &cl) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const float lam = ld.x, delta = ld.y;
-  const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 16));
-  const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 48));
-  const float mid = (lane < 32) ? m0 : m1;
-  if (tid < Q) {
-    cl.lam[tid] = lam;
-    cl.delta[tid] = delta;
-    cl.w[tid] = fast_exp2(lend2 - lam) * delta;
-    cl.u[tid] = fast_exp2(mid - lam) * delta;
-    if ((lane & 31) == 16) cl.mid[tid >> 5] = lam;
+__device__ __forceinline__ void stage_dt(float v, ChunkLds<Q> &cl) {
+  if (threadIdx.x < (unsigned)Q) cl.dts[threadIdx.x] = v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves:
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row 0's total added
+// to row 1 and row 2's to row 3 (row_bcast:15), then rows 0-1's total to
+// rows 2-3 (row_bcast:31).  Lanes a move does not reach add zero.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int t;
+  const int x = __float_as_int(v);
+  switch (ctrl_sel) {
+    case 0: t = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true); break;  // row_shr:1
+    case 1: t = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true); break;  // row_shr:2
+    case 2: t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true); break;  // row_shr:4
+    case 3: t = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true); break;  // row_shr:8
+    case 4: t = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); break; // row_bcast:15
+    default: t = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); break; // row_bcast:31
+  }
+  return v + __int_as_float(t);
+}
+
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+#pragma unroll
+  for (int k = 0; k < 6; ++k) v = dpp_add(v, k);
+  return v;
+}
+
+// Discretise and scan the chunk starting at token t0, then fill its LDS
+// scalars (the caller puts a barrier before any reader).  Returns Lam_end and
+// whether |delta*A| <= 7 (log2 units) for every token, which keeps the
+// factored intra-chunk decay of the main pass inside fp32 range.
+template <int Q>
+__device__ __forceinline__ void chunk_prep(const Params &p, uint32_t t0,
+                                           float a_h, float bias, ChunkLds<Q> &cl, float &lend,
+                                           bool &factored) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float lam[Q / 64], del[Q / 64];
+  float run = 0.f;
+  bool big = false;
+#pragma unroll
+  for (int m = 0; m < Q / 64; ++m) {
+    float u = cl.dts[lane + 64 * m] + bias;
+    if (p.dt_softplus) u = (u > 20.f) ? u : __logf(1.f + __expf(u));
+    const float delta = (t0 + lane + 64 * m < (uint64_t)p.L) ? fminf(fmaxf(u, p.dt_min), p.dt_max) : 0.f;
+    const float a = delta * a_h * kLog2e;
+    big |= fabsf(a) > 7.f;
+    const float v = wave_inclusive_sum(a);
+    lam[m] = v + run;
+    del[m] = delta;
+    run += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  }
+  lend = run;
+  factored = __ballot(big) == 0;
+  // wave w < Q/64 writes the records of tokens 64 w .. 64 w + 63
+  if (w < Q / 64) {
+    float lm = 0.f, dl = 0.f;
+#pragma unroll
+    for (int m = 0; m < Q / 64; ++m)
+      if (m == w) {
+        lm = lam[m];
+        dl = del[m];
+      }
+    const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lm), 16));
+    const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lm), 48));
+    const float mid = (lane < 32) ? m0 : m1;
+    const int t = 64 * w + lane;
+    cl.lam[t] = lm;
+    cl.delta[t] = dl;
+    cl.w[t] = fast_exp2(lend - lm) * dl;
+    cl.u[t] = fast_exp2(mid - lm) * dl;
+    if ((lane & 31) == 16) cl.mid[t >> 5] = lm;
   }
 }
 
@@ -566,21 +582,21 @@ __global__ __launch_bounds__(512, F32 ? 2 : 4) void ssd_group_state_kernel(Param
   const int64_t c_begin = j * p.cpg, c_end = c_begin + p.cpg;  // never the last group
   auto qc_of = [&](int64_t c) { return (int)((p.L - c * Q) < Q ? (p.L - c * Q) : Q); };
 
+  const rsrc_t rdt = make_rsrc(p.dt + b * p.L * p.H, (uint32_t)(p.L * p.H * 4));
+  const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
   BlockRaw<N, IO, T> nxt;
   load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), nxt);
-  float2 ldv = load_lamd<Q, T>(p, bh, c_begin);
-  float2 civ = p.cinfo[bh * p.nc + c_begin];
+  // dt two chunks ahead in registers, one chunk ahead in LDS
+  stage_dt<Q>(load_dt(rdt, sv.H, sv.h, (uint32_t)(c_begin * Q), Q), clb[c_begin & 1]);
+  float dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c_begin + 1 < c_end ? c_begin + 1 : c_begin) * Q), Q);
+  lds_barrier();
   for (int64_t c = c_begin; c < c_end; ++c) {
     const uint32_t t0 = (uint32_t)(c * Q);
     const int Qc = qc_of(c);
     ChunkLds<Q> &cl = clb[c & 1];
-    const float lend2 = civ.x;
-    chunk_prep<Q>(ldv, lend2, cl);
-    {
-      const int64_t cn = (c + 1 < c_end) ? c + 1 : c;
-      ldv = load_lamd<Q, T>(p, bh, cn);
-      civ = p.cinfo[bh * p.nc + cn];
-    }
+    float lend2;
+    bool factored;
+    chunk_prep<Q>(p, t0, a_h, bias, cl, lend2, factored);
     const float dec = fast_exp2(lend2);
 #pragma unroll
     for (int t = 0; t < NN; ++t) sacc[t] *= dec;
@@ -589,6 +605,11 @@ __global__ __launch_bounds__(512, F32 ? 2 : 4) void ssd_group_state_kernel(Param
     for (int jb = 0; jb < nb; ++jb) {
       lds_barrier();
       store_block<N, F32, IO, T, false>(nxt, jb, cl.w, nullptr, sBT, sXT);
+      if (jb == 0) {
+        // chunk c-1's readers of the other buffer passed the barrier above
+        stage_dt<Q>(dtr, clb[(c + 1) & 1]);
+        dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c + 2 < c_end ? c + 2 : c) * Q), Q);
+      }
       lds_barrier();
       // next block: the chunk's next one, else the next chunk's first, else
       // (last block of the group) this one again, unused
@@ -674,8 +695,11 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   };
   load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), nxt);
   load_zb((uint32_t)(c_begin * Q));
-  float2 ldv = load_lamd<Q, T>(p, bh, c_begin);
-  float2 civ = p.cinfo[bh * p.nc + c_begin];
+  const rsrc_t rdt = make_rsrc(p.dt + b * p.L * p.H, (uint32_t)(p.L * p.H * 4));
+  const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
+  // dt two chunks ahead in registers, one chunk ahead in LDS
+  stage_dt<Q>(load_dt(rdt, sv.H, sv.h, (uint32_t)(c_begin * Q), Q), clb[c_begin & 1]);
+  float dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c_begin + 1 < c_end ? c_begin + 1 : c_begin) * Q), Q);
   typename IO::raw8 craw[NR][KB];
   auto load_c = [&](uint32_t t0) {
 #pragma unroll
@@ -709,21 +733,20 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sS[SS::row(r) * LDN + SS::col(t)] = (E)sacc[t][r];
   }
+  lds_barrier();  // the first chunk's staged dt
 
   for (int64_t c = c_begin; c < c_end; ++c) {
     const uint32_t t0 = (uint32_t)(c * Q);
     const int Qc = qc_of(c);
     ChunkLds<Q> &cl = clb[c & 1];
     if (!kPrefetchC) load_c(t0);
-    const float lend2 = civ.x;
-    const bool factored = civ.y != 0.f;
-    chunk_prep<Q>(ldv, lend2, cl);
+    float lend2;
+    bool factored;
+    chunk_prep<Q>(p, t0, a_h, bias, cl, lend2, factored);
     lds_barrier();
-    {
-      const int64_t cn = (c + 1 < c_end) ? c + 1 : c;
-      ldv = load_lamd<Q, T>(p, bh, cn);
-      civ = p.cinfo[bh * p.nc + cn];
-    }
+    // chunk c-1's readers of the other buffer passed the barrier above
+    stage_dt<Q>(dtr, clb[(c + 1) & 1]);
+    dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c + 2 < c_end ? c + 2 : c) * Q), Q);
 
     // B operand of B.C^T and A operand of C.S^T share this layout
     frag cfr[NR][KB];
@@ -934,13 +957,12 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool is_supported_chunk(int64_t q) { return q == 64 || q == 128 || q == 256; }
 
-// Workspace: per-token {Lam, delta} records and per-chunk {Lam_end, flag}
-// written by chunk_cumsum, then (with several chunk groups) the group states
-// and group decays.
+// Workspace (only when a sequence is cut into several chunk groups): the
+// group states and group decays.
 struct Plan {
   int64_t nc, cpg, ngroups;
-  size_t lamd_bytes, cinfo_bytes, state_bytes, lam_bytes;
-  size_t total() const { return lamd_bytes + cinfo_bytes + state_bytes + lam_bytes; }
+  size_t state_bytes, lam_bytes;
+  size_t total() const { return state_bytes + lam_bytes; }
 };
 
 // Validation of everything but pointers.
@@ -999,8 +1021,6 @@ Plan make_plan(const ssd_desc *d, int64_t chunk) {
   pl.cpg = cpg;
   pl.ngroups = (pl.nc + cpg - 1) / cpg;
   const int64_t slots = bh * (pl.ngroups - 1);
-  pl.lamd_bytes = align_up((size_t)(bh * pl.nc * chunk) * 2 * sizeof(float));
-  pl.cinfo_bytes = align_up((size_t)(bh * pl.nc) * 2 * sizeof(float));
   pl.state_bytes = align_up((size_t)slots * (size_t)(d->headdim * d->dstate) * sizeof(float));
   pl.lam_bytes = align_up((size_t)slots * sizeof(float));
   if (slots == 0) pl.state_bytes = pl.lam_bytes = 0;
@@ -1009,11 +1029,10 @@ Plan make_plan(const ssd_desc *d, int64_t chunk) {
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+
 template <int Q, int N, bool F32, class IO>
 ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, const ssd_desc *d) {
   const int64_t bh = prm.batch * prm.H;
-  hipLaunchKernelGGL(ssd_chunk_cumsum_kernel<Q>, dim3((unsigned)(bh * pl.nc)), dim3(Q), 0, stream,
-                     prm);
   if (pl.ngroups > 1) {
     const int64_t t1 = bh * (pl.ngroups - 1);
     const int64_t g1 = 8 * ((t1 + 7) / 8);
@@ -1115,7 +1134,7 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B
     return SSD_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, chunk);
   const size_t need = pl.total();
-  if (!d->workspace || d->workspace_bytes < need || !aligned16(d->workspace))
+  if (need > 0 && (!d->workspace || d->workspace_bytes < need || !aligned16(d->workspace)))
     return SSD_ERR_WORKSPACE;
 
   Params prm;
@@ -1132,11 +1151,8 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B
   prm.out = out;
   prm.final_state = final_state;
   char *ws = static_cast<char *>(d->workspace);
-  prm.lamd = reinterpret_cast<float2 *>(ws);
-  prm.cinfo = reinterpret_cast<float2 *>(ws + pl.lamd_bytes);
-  prm.grp_state = pl.state_bytes ? reinterpret_cast<float *>(ws + pl.lamd_bytes + pl.cinfo_bytes) : nullptr;
-  prm.grp_lam = pl.lam_bytes ? reinterpret_cast<float *>(ws + pl.lamd_bytes + pl.cinfo_bytes + pl.state_bytes)
-                             : nullptr;
+  prm.grp_state = pl.state_bytes ? reinterpret_cast<float *>(ws) : nullptr;
+  prm.grp_lam = pl.lam_bytes ? reinterpret_cast<float *>(ws + pl.state_bytes) : nullptr;
   prm.batch = d->batch;
   prm.L = d->seqlen;
   prm.H = d->nheads;

@@ -154,6 +154,36 @@ def test_guard_bands_untouched(gpu_lib):
     assert_close(fin.cpu().numpy(), ref_fin, TOL["f16"], "final_state")
 
 
+@pytest.mark.parametrize("N", [64, 128])
+def test_workspace_reuse_and_stale_contents(gpu_lib, N):
+    """Many chunk groups (one chunk each); the workspace starts as garbage and
+    is then reused by calls with other inputs: nothing a call reads from it
+    may depend on what an earlier call left there."""
+    _say(f"[case] workspace reuse N={N}")
+    d1 = random_inputs(2, 1300, 3, 64, N, 1, seed=500 + N, has_D=True, has_h0=True)
+    d2 = random_inputs(2, 1300, 3, 64, N, 1, seed=600 + N, has_h0=True)
+    g1, g2 = to_gpu(d1), to_gpu(d2)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def prep(g, ws):
+        return gpu_lib.prepare(g["x"], g["dt"], g["A"], g["B"], g["C"], 64, D=g["D"],
+                               initial_states=g["initial_states"], dt_softplus=True,
+                               return_final_state=True, chunks_per_wg=1, workspace=ws)
+
+    call1, out1, fin1, ws = prep(g1, None)
+    assert ws is not None and gpu_lib.plan(call1.desc, 64) == (1, 21)
+    ws.fill_(255)
+    ref1, ref2 = oracle_run(d1), oracle_run(d2)
+    call2, out2, fin2, _ = prep(g2, ws)
+    for k, (call, out, fin, ref) in enumerate([(call1, out1, fin1, ref1), (call2, out2, fin2, ref2),
+                                               (call1, out1, fin1, ref1)]):
+        out.fill_(float("nan"))
+        call.launch(st)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ref[0], TOL["f16"], f"out (call {k})")
+        assert_close(fin.cpu().numpy(), ref[1], TOL["f16"], f"final_state (call {k})")
+
+
 def test_invalid_calls_raise(gpu_lib):
     d = to_gpu(random_inputs(1, 64, 2, 64, 64, 1, seed=404))
     with pytest.raises(NotImplementedError):
