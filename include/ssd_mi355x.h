@@ -44,8 +44,12 @@ typedef enum {
                                final_state NULL while requested       */
   SSD_ERR_UNSUPPORTED = 2,  /* valid but not compiled: headdim != 64,
                                dstate not in {64,128}, chunk not in
-                               {64,128,256}                           */
-  SSD_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than required */
+                               {64,128,256}, fp16 storage, or one batch
+                               row of x/z/out or of B/C reaching 2 GiB
+                               (rows are addressed with 32-bit offsets) */
+  SSD_ERR_WORKSPACE = 3,    /* the plan needs a workspace and it is NULL,
+                               smaller than required or not 16-byte
+                               aligned                                */
   SSD_ERR_LAUNCH = 4        /* the HIP runtime rejected a launch       */
 } ssd_status;
 
@@ -76,7 +80,11 @@ typedef struct ssd_desc {
   const void *z;             /* [B,L,H,P] gate, or NULL (no gate)            */
   const float *dt_bias;      /* [H] fp32, or NULL (zero)                      */
   const float *initial_state;/* [B,H,P,N] fp32, or NULL (zero state)          */
-  void *workspace;           /* device scratch owned by the caller            */
+  void *workspace;           /* device scratch owned by the caller (NULL when
+                                ssd_fwd_workspace_size reports 0).  Its
+                                contents need no initialisation and mean
+                                nothing after the call; calls that may run
+                                at the same time must not share it           */
   size_t workspace_bytes;    /* its size; see ssd_fwd_workspace_size          */
   int32_t chunks_per_wg;     /* chunks one workgroup walks in sequence; 0 picks
                                 automatically (see ssd_fwd_plan)              */
