@@ -236,15 +236,22 @@ template <int Q> struct ChunkLds {
 // delta = clamp(softplus(dt + dt_bias)) (0 past the sequence end) and the
 // inclusive in-chunk prefix Lam of delta*A in log2 units (a wavefront scan
 // per 64 tokens plus the running total of the earlier ones).
-// Threads past Q re-load token Q-1 (unused): the load stays unconditional.
+// Thread t < Q handles token t; threads past Q load token Q-1 again (one
+// merged request per wave) and store that same value over it, which keeps
+// the load and the LDS store free of branches (a branch here makes the
+// compiler wait for every load in flight).
+__device__ __forceinline__ uint32_t dt_token(int Q) {
+  return threadIdx.x < (uint32_t)Q ? threadIdx.x : (uint32_t)Q - 1;
+}
+
 __device__ __forceinline__ float load_dt(rsrc_t rdt, uint32_t H, uint32_t h, uint32_t t0, int Q) {
-  const uint32_t i = threadIdx.x < (uint32_t)Q ? threadIdx.x : (uint32_t)Q - 1;
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, ((t0 + i) * H + h) * 4, 0, 0));
+  return __uint_as_float(
+      __builtin_amdgcn_raw_buffer_load_b32(rdt, ((t0 + dt_token(Q)) * H + h) * 4, 0, 0));
 }
 
 template <int Q>
 __device__ __forceinline__ void stage_dt(float v, ChunkLds<Q> &cl) {
-  if (threadIdx.x < (unsigned)Q) cl.dts[threadIdx.x] = v;
+  cl.dts[dt_token(Q)] = v;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves:
@@ -557,10 +564,12 @@ __device__ __forceinline__ int nblocks(int Qc) { return (Qc + kJB - 1) / kJB; }
 
 // First pass (only when a sequence is split into several chunk groups): the
 // state each of the first ngroups-1 groups builds from a zero start, and the
-// group's total decay.  Blocks of B and x are prefetched one ahead.
+// group's total decay.  Four waves walk the group's 64-token blocks (all its
+// chunks are full) with two blocks of B and x in flight: a block's buffer is
+// refilled with the block two ahead as soon as it is staged in LDS.
 template <int Q, int N, bool F32, class IO>
-__global__ __launch_bounds__(512, F32 ? 2 : 4) void ssd_group_state_kernel(Params p) {
-  constexpr int W = 8, T = 64 * W;
+__global__ __launch_bounds__(256) void ssd_group_state_kernel(Params p) {
+  constexpr int W = 4, T = 64 * W, NB = Q / kJB;
   using E = typename Mma<F32>::T;
   using SS = StateSplit<N, W>;
   constexpr int LDJ = kJB + 8;
@@ -578,47 +587,64 @@ __global__ __launch_bounds__(512, F32 ? 2 : 4) void ssd_group_state_kernel(Param
   f32x4 sacc[NN];
 #pragma unroll
   for (int t = 0; t < NN; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float lgrp = 0.f;
+  float lgrp = 0.f, lend2 = 0.f;
   const int64_t c_begin = j * p.cpg, c_end = c_begin + p.cpg;  // never the last group
-  auto qc_of = [&](int64_t c) { return (int)((p.L - c * Q) < Q ? (p.L - c * Q) : Q); };
+  const int nblk = (int)p.cpg * NB;
+  const uint32_t tg = (uint32_t)(c_begin * Q);
+  auto tok = [&](int i) { return tg + (uint32_t)(kJB * (i < nblk ? i : nblk - 1)); };
 
   const rsrc_t rdt = make_rsrc(p.dt + b * p.L * p.H, (uint32_t)(p.L * p.H * 4));
   const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
-  BlockRaw<N, IO, T> nxt;
-  load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), nxt);
-  // dt two chunks ahead in registers, one chunk ahead in LDS
-  stage_dt<Q>(load_dt(rdt, sv.H, sv.h, (uint32_t)(c_begin * Q), Q), clb[c_begin & 1]);
-  float dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c_begin + 1 < c_end ? c_begin + 1 : c_begin) * Q), Q);
+  // Each block buffer also carries the raw dt of the block one chunk later
+  // (token 64 k + t of the group for block k + NB, thread t < 64; later
+  // threads repeat token 63); it is staged in the next chunk's LDS scalars
+  // when the block is staged, so its wait is the block's own.  The first
+  // chunk's dt is staged up front.
+  auto load_bdt = [&](int k) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        rdt, ((tg + (uint32_t)(kJB * k) + dt_token(kJB)) * sv.H + sv.h) * 4, 0, 0));
+  };
+  stage_dt<Q>(load_dt(rdt, sv.H, sv.h, tg, Q), clb[c_begin & 1]);
+  // (scheduling barriers keep every buffer's loads in the same issue order
+  // before and inside the loop, so the compiler can count them exactly)
+  BlockRaw<N, IO, T> nx0, nx1;
+  load_block<N, IO, T>(sv, tok(0), nx0);
+  float bdt0 = load_bdt(NB);
+  __builtin_amdgcn_sched_barrier(0);
+  load_block<N, IO, T>(sv, tok(1), nx1);
+  float bdt1 = load_bdt(1 + NB);
+  __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    const uint32_t t0 = (uint32_t)(c * Q);
-    const int Qc = qc_of(c);
+
+  auto step = [&](BlockRaw<N, IO, T> &buf, float &bdt, int i) {
+    const int jb = i % NB;
+    const int64_t c = c_begin + i / NB;
     ChunkLds<Q> &cl = clb[c & 1];
-    float lend2;
-    bool factored;
-    chunk_prep<Q>(p, t0, a_h, bias, cl, lend2, factored);
-    const float dec = fast_exp2(lend2);
+    if (jb == 0) {
+      bool factored;
+      chunk_prep<Q>(p, (uint32_t)(c * Q), a_h, bias, cl, lend2, factored);
+      const float dec = fast_exp2(lend2);
 #pragma unroll
-    for (int t = 0; t < NN; ++t) sacc[t] *= dec;
-    lgrp += lend2;
-    const int nb = nblocks(Qc);
-    for (int jb = 0; jb < nb; ++jb) {
-      lds_barrier();
-      store_block<N, F32, IO, T, false>(nxt, jb, cl.w, nullptr, sBT, sXT);
-      if (jb == 0) {
-        // chunk c-1's readers of the other buffer passed the barrier above
-        stage_dt<Q>(dtr, clb[(c + 1) & 1]);
-        dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c + 2 < c_end ? c + 2 : c) * Q), Q);
-      }
-      lds_barrier();
-      // next block: the chunk's next one, else the next chunk's first, else
-      // (last block of the group) this one again, unused
-      const uint32_t tn = (jb + 1 < nb) ? t0 + kJB * (jb + 1)
-                                        : (c + 1 < c_end) ? t0 + Q : t0 + kJB * jb;
-      load_block<N, IO, T>(sv, tn, nxt);
-      state_block_mma<N, F32, W>(sXT, sBT, sacc);
+      for (int t = 0; t < NN; ++t) sacc[t] *= dec;
+      lgrp += lend2;
     }
+    lds_barrier();
+    store_block<N, F32, IO, T, false>(buf, jb, cl.w, nullptr, sBT, sXT);
+    // dt of the same block position in chunk c+1, into the other buffer
+    // (its readers from chunk c-1 passed the barrier above)
+    clb[(c + 1) & 1].dts[kJB * jb + dt_token(kJB)] = bdt;
+    lds_barrier();
+    load_block<N, IO, T>(sv, tok(i + 2), buf);  // past the group's end: its last block, unused
+    bdt = load_bdt(i + 2 + NB);
+    __builtin_amdgcn_sched_barrier(0);
+    state_block_mma<N, F32, W>(sXT, sBT, sacc);
+  };
+  int i = 0;
+  for (; i + 1 < nblk; i += 2) {
+    step(nx0, bdt0, i);
+    step(nx1, bdt1, i + 1);
   }
+  if (i < nblk) step(nx0, bdt0, i);
   const int64_t slot = bh * (p.ngroups - 1) + j;
   float *dst = p.grp_state + slot * (int64_t)(kP * N);
 #pragma unroll
@@ -1036,7 +1062,7 @@ ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, con
   if (pl.ngroups > 1) {
     const int64_t t1 = bh * (pl.ngroups - 1);
     const int64_t g1 = 8 * ((t1 + 7) / 8);
-    hipLaunchKernelGGL((ssd_group_state_kernel<Q, N, F32, IO>), dim3((unsigned)g1), dim3(512),
+    hipLaunchKernelGGL((ssd_group_state_kernel<Q, N, F32, IO>), dim3((unsigned)g1), dim3(256),
                        0, stream, prm);
     const int PN = kP * N;
     hipLaunchKernelGGL(ssd_group_passing_kernel, dim3((unsigned)(bh * (PN / 256))), dim3(256), 0,
