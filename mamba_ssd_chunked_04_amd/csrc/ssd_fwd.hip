@@ -12,14 +12,16 @@
 //                        + exp(Lam_i) C_i . S_in[c]  + D x_i,  then * silu(z_i)
 //
 // MI355X design (not the Ascend Cube/Vector split of the pages):
-//   * one workgroup (4 wave64s) walks `cpg` consecutive chunks of one (b, h),
-//     keeping the P x N state in MFMA accumulators across chunks, so the
-//     state recurrence costs no HBM traffic inside a chunk group;
+//   * one workgroup (4 or 8 wave64s) walks `cpg` consecutive chunks of one
+//     (b, h), keeping the P x N state in MFMA accumulators across chunks, so
+//     the state recurrence costs no HBM traffic inside a chunk group;
+//   * chunk_cumsum runs inside the matrix passes, at the start of each chunk;
 //   * when (b, h) pairs alone cannot fill 256 CUs, the sequence is cut into
 //     chunk groups: a first pass (ssd_group_state_kernel) builds each
-//     group's state from zero, a light elementwise sweep
-//     (ssd_group_passing_kernel) chains them, and the main pass
-//     (ssd_chunk_scan_kernel) starts every group from its entering state;
+//     group's state from zero, and the main pass (ssd_chunk_scan_kernel)
+//     chains the aggregates of the groups before its own (state_passing)
+//     to start every group from its entering state (with many groups a
+//     separate elementwise pass, ssd_group_passing_kernel, chains them once);
 //   * all contractions (C.B^T, M.X, C.S^T, X^T.diag(w).B) are
 //     v_mfma_f32_16x16x32_f16 tiles (or 16x16x4 fp32 on the check path) with
 //     B, X staged in LDS 64 tokens at a time and C held in registers;
@@ -163,19 +165,22 @@ struct Params {
   const float *h0;
   void *out;
   float *final_state;
-  float *grp_state;  // [B*H][ngroups-1][P*N]: group aggregates, then entering states
+  float *grp_state;  // [B*H][ngroups-1][P*N]: group aggregates (state from a zero
+                     // start), or entering states once the passing pass ran
   float *grp_lam;    // [B*H][ngroups-1]: group total log2-decay
   int64_t batch, L, H, G, nc, ngroups, cpg;
   float dt_min, dt_max;
   int dt_softplus, z_bf16, out_bf16, ret_final;
+  int chained;  // grp_state holds entering states (the passing pass ran)
 };
 
 // Workgroup id -> (b, h, chunk group).  Tiles are ordered (b, group, g, head
 // in group) and dealt in contiguous runs to the 8 XCDs (workgroup n runs on
 // XCD n % 8), so the heads that share one B/C group run side by side on one
-// XCD and share its L2.
+// XCD and share its L2.  With `late_first` the chunk groups are dealt from
+// the last one down (later groups have more to do before their first chunk).
 __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_here, int64_t &b,
-                                            int64_t &h, int64_t &j) {
+                                            int64_t &h, int64_t &j, bool late_first = false) {
   const int64_t total = p.batch * p.H * ngroups_here;
   const int64_t n = blockIdx.x;
   const int64_t per = (total + 7) / 8;
@@ -187,6 +192,7 @@ __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_her
   const int64_t g = rest % p.G;
   rest /= p.G;
   j = rest % ngroups_here;
+  if (late_first) j = ngroups_here - 1 - j;
   b = rest / ngroups_here;
   h = g * hpg + hh;
   return true;
@@ -563,8 +569,8 @@ __device__ __forceinline__ int nblocks(int Qc) { return (Qc + kJB - 1) / kJB; }
 // ---------------------------------------------------------------- kernels
 
 // First pass (only when a sequence is split into several chunk groups): the
-// state each of the first ngroups-1 groups builds from a zero start, and the
-// group's total decay.  Four waves walk the group's 64-token blocks (all its
+// state each of the first ngroups-1 groups builds from a zero start (its
+// aggregate), and the group's total decay.  Four waves walk the group's 64-token blocks (all its
 // chunks are full) with two blocks of B and x in flight: a block's buffer is
 // refilled with the block two ahead as soon as it is staged in LDS.
 template <int Q, int N, bool F32, class IO>
@@ -654,7 +660,8 @@ __global__ __launch_bounds__(256) void ssd_group_state_kernel(Params p) {
   if (threadIdx.x == 0) p.grp_lam[slot] = lgrp;
 }
 
-// state_passing across chunk groups (elementwise over P*N, sequential over
+// state_passing across chunk groups as its own pass (used when sequences
+// have more than kFoldGroups+1 groups; elementwise over P*N, sequential over
 // groups): S = exp(Lam_grp) S + S_grp; slot j is overwritten with the state
 // entering group j+1.
 __global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p, int PN) {
@@ -695,7 +702,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) ChunkLds<Q> clb[2];
 
   int64_t b, h, j;
-  if (!decode_tile(p, p.ngroups, b, h, j)) return;
+  if (!decode_tile(p, p.ngroups, b, h, j, true)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lq = lane >> 4;
   const int pt0 = RS::pt0(w);
   const int64_t g = h / (p.H / p.G);
@@ -739,21 +746,46 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   constexpr bool kPrefetchC = NR * KB * sizeof(typename IO::raw8) <= 64;
   if (kPrefetchC) load_c((uint32_t)(c_begin * Q));
 
-  // state entering this group: h0 / zero for the first, the chained group
-  // state otherwise
-  // (all loads issued before any is used; a null start reads as zeros
-  // through an empty buffer range)
+  // state entering this group: state_passing over the groups before it,
+  // S = exp(Lam_grp[i]) S + S_grp[i] for i < j starting from h0 (or zero),
+  // elementwise in this thread's share of the state; the aggregates are
+  // loaded R at a time (a missing h0 reads as zeros through an empty range).
+  // When the passing pass already chained the groups, slot j-1 holds the
+  // entering state: the same loop then runs once, from zero.
   f32x4 sacc[NN];
   {
-    const float *init = (j == 0) ? (p.h0 ? p.h0 + bh * (int64_t)(kP * N) : nullptr)
-                                 : p.grp_state + (bh * (p.ngroups - 1) + (j - 1)) * (int64_t)(kP * N);
-    const rsrc_t ri = make_rsrc(init, init ? (uint32_t)(kP * N * 4) : 0u);
+    const bool from_zero = p.chained && j > 0;
+    const int64_t i_begin = from_zero ? j - 1 : 0;
+    const float *h0 = (p.h0 && !from_zero) ? p.h0 + bh * (int64_t)(kP * N) : nullptr;
+    const rsrc_t ri = make_rsrc(h0, h0 ? (uint32_t)(kP * N * 4) : 0u);
 #pragma unroll
     for (int t = 0; t < NN; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         sacc[t][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
             ri, (uint32_t)(SS::row(r) * N + SS::col(t)) * 4, 0, 0));
+    constexpr int R = 16 / NN > 0 ? 16 / NN : 1;
+    const int64_t ng1 = p.ngroups - 1;
+    const float *agg = p.grp_state + bh * ng1 * (int64_t)(kP * N);
+    const float *glam = p.grp_lam + bh * ng1;
+    for (int64_t i0 = i_begin; i0 < j; i0 += R) {
+      f32x4 v[R][NN];
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        const int64_t i = (i0 + q < j) ? i0 + q : j - 1;
+#pragma unroll
+        for (int t = 0; t < NN; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[q][t][r] = agg[i * (kP * N) + SS::row(r) * N + SS::col(t)];
+      }
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        if (i0 + q >= j) break;
+        const float dec = fast_exp2(glam[i0 + q]);
+#pragma unroll
+        for (int t = 0; t < NN; ++t) sacc[t] = dec * sacc[t] + v[q][t];
+      }
+    }
 #pragma unroll
     for (int t = 0; t < NN; ++t)
 #pragma unroll
@@ -983,6 +1015,11 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool is_supported_chunk(int64_t q) { return q == 64 || q == 128 || q == 256; }
 
+// The main pass chains up to this many group aggregates itself; with more
+// groups a separate passing pass chains them once (measured: 8 aggregates
+// per workgroup cost less than the extra pass, 15 cost more).
+constexpr int64_t kFoldGroups = 8;
+
 // Workspace (only when a sequence is cut into several chunk groups): the
 // group states and group decays.
 struct Plan {
@@ -1064,9 +1101,11 @@ ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, con
     const int64_t g1 = 8 * ((t1 + 7) / 8);
     hipLaunchKernelGGL((ssd_group_state_kernel<Q, N, F32, IO>), dim3((unsigned)g1), dim3(256),
                        0, stream, prm);
-    const int PN = kP * N;
-    hipLaunchKernelGGL(ssd_group_passing_kernel, dim3((unsigned)(bh * (PN / 256))), dim3(256), 0,
-                       stream, prm, PN);
+    if (prm.chained) {
+      const int PN = kP * N;
+      hipLaunchKernelGGL(ssd_group_passing_kernel, dim3((unsigned)(bh * (PN / 256))), dim3(256), 0,
+                         stream, prm, PN);
+    }
   }
   const int64_t t2 = bh * pl.ngroups;
   const int64_t g2 = 8 * ((t2 + 7) / 8);
@@ -1192,6 +1231,7 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B
   prm.z_bf16 = d->z_dtype == SSD_BF16;
   prm.out_bf16 = d->out_dtype == SSD_BF16;
   prm.ret_final = return_final_state ? 1 : 0;
+  prm.chained = pl.ngroups - 1 > kFoldGroups;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (chunk) {

@@ -115,6 +115,19 @@ def test_short_and_ragged_sequences(gpu_lib, L):
         assert_close(fin, ref_fin, TOL["f16"], f"final Q={Q}")
 
 
+@pytest.mark.parametrize("ngroups", [9, 10])
+def test_group_chaining_either_side_of_the_fold_limit(gpu_lib, ngroups):
+    """One chunk per group: 9 groups are chained inside the main pass (8
+    aggregates before the last), 10 by the separate passing pass."""
+    _say(f"[case] {ngroups} chunk groups")
+    d = random_inputs(1, 64 * ngroups - 17, 3, 64, 128, 1, seed=700 + ngroups, has_D=True,
+                      has_h0=True)
+    ref_out, ref_fin = oracle_run(d)
+    out, fin = gpu_run(gpu_lib, d, 64, chunks_per_wg=1)
+    assert_close(out, ref_out, TOL["f16"], "out")
+    assert_close(fin, ref_fin, TOL["f16"], "final_state")
+
+
 def test_no_final_state_and_bf16_out(gpu_lib):
     d = random_inputs(1, 200, 2, 64, 128, 1, seed=401, has_z=True)
     ref_out, _ = oracle_run(d)
