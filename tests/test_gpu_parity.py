@@ -197,6 +197,38 @@ def test_workspace_reuse_and_stale_contents(gpu_lib, N):
         assert_close(fin.cpu().numpy(), ref[1], TOL["f16"], f"final_state (call {k})")
 
 
+@pytest.mark.parametrize("cpw", [0, 1])
+def test_graph_capture_replays_match_eager(gpu_lib, cpw):
+    """One call captured in a HIP graph (the entry point allocates and
+    synchronises nothing) and replayed several times with other eager work
+    in between; every replay must equal the eager result bit for bit."""
+    _say(f"[case] graph capture chunks_per_wg={cpw}")
+    d = to_gpu(random_inputs(2, 900, 4, 64, 128, 2, seed=800 + cpw, has_D=True, has_z=True,
+                             has_h0=True))
+    s = torch.cuda.Stream()
+    call, out, fin, ws = gpu_lib.prepare(d["x"], d["dt"], d["A"], d["B"], d["C"], 128, D=d["D"],
+                                         z=d["z"], initial_states=d["initial_states"],
+                                         dt_softplus=True, return_final_state=True,
+                                         chunks_per_wg=cpw)
+    with torch.cuda.stream(s):
+        call.launch(s.cuda_stream)
+    torch.cuda.synchronize()
+    ref_out, ref_fin = out.clone(), fin.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call.launch(s.cuda_stream)
+    for k in range(4):
+        out.fill_(float("nan"))
+        fin.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {k}: out differs"
+        assert torch.equal(fin, ref_fin), f"replay {k}: final_state differs"
+        del junk
+
+
 def test_invalid_calls_raise(gpu_lib):
     d = to_gpu(random_inputs(1, 64, 2, 64, 64, 1, seed=404))
     with pytest.raises(NotImplementedError):
