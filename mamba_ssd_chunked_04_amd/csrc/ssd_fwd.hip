@@ -518,6 +518,33 @@ struct StateSplit {
   }
 };
 
+// Main-pass waves per workgroup for a chunk size.
+template <int Q> constexpr int main_waves() { return Q == 256 ? 8 : 4; }
+
+// Group records in the workspace (aggregates, entering states) are kept in
+// the main pass's register order: slice t (of NN) of main-pass thread i, the
+// four rows row(0..3) of column col(t), sits at float (t * T + i) * 4 (T
+// main-pass threads), so each slice of a record is one coalesced 16-byte
+// load per lane.  rec_index maps the element (row p, column n) of the P x N
+// state to its position; rec_element is the inverse.
+template <int N, int WM>
+__device__ __forceinline__ uint32_t rec_index(int row, int col) {
+  constexpr int NN = StateSplit<N, WM>::NN, T = 64 * WM;
+  const int tile = col >> 4;
+  const int w = 4 * (tile / NN) + (row >> 4);
+  const int tid = 64 * w + 16 * ((row & 15) >> 2) + (col & 15);
+  return (uint32_t)(((tile % NN) * T + tid) * 4 + (row & 3));
+}
+
+template <int N, int WM>
+__device__ __forceinline__ void rec_element(uint32_t e, int &row, int &col) {
+  constexpr int NN = StateSplit<N, WM>::NN, T = 64 * WM;
+  const int r = (int)(e & 3), t = (int)((e >> 2) / T), tid = (int)((e >> 2) % T);
+  const int w = tid >> 6, lane = tid & 63;
+  row = 16 * (w & 3) + 4 * (lane >> 4) + r;
+  col = 16 * ((w >> 2) * NN + t) + (lane & 15);
+}
+
 // chunk_state on one staged block: S += X^T diag(w) B over the block's 64
 // tokens, for this wave's share of the state.
 template <int N, bool F32, int W>
@@ -651,12 +678,20 @@ __global__ __launch_bounds__(256) void ssd_group_state_kernel(Params p) {
     step(nx1, bdt1, i + 1);
   }
   if (i < nblk) step(nx0, bdt0, i);
+  // the aggregate, in the main pass's register order
   const int64_t slot = bh * (p.ngroups - 1) + j;
   float *dst = p.grp_state + slot * (int64_t)(kP * N);
+  constexpr int WM = main_waves<Q>();
+  if (WM == W) {
 #pragma unroll
-  for (int t = 0; t < NN; ++t)
+    for (int t = 0; t < NN; ++t)
+      *reinterpret_cast<f32x4 *>(dst + (t * T + threadIdx.x) * 4) = sacc[t];
+  } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[SS::row(r) * N + SS::col(t)] = sacc[t][r];
+    for (int t = 0; t < NN; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[rec_index<N, WM>(SS::row(r), SS::col(t))] = sacc[t][r];
+  }
   if (threadIdx.x == 0) p.grp_lam[slot] = lgrp;
 }
 
@@ -664,11 +699,18 @@ __global__ __launch_bounds__(256) void ssd_group_state_kernel(Params p) {
 // have more than kFoldGroups+1 groups; elementwise over P*N, sequential over
 // groups): S = exp(Lam_grp) S + S_grp; slot j is overwritten with the state
 // entering group j+1.
-__global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p, int PN) {
-  const int64_t blocks_per_bh = PN / 256;
+template <int N, int WM>
+__global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p) {
+  constexpr int PN = kP * N;
+  constexpr int64_t blocks_per_bh = PN / 256;
   const int64_t bh = blockIdx.x / blocks_per_bh;
-  const int64_t e = (blockIdx.x % blocks_per_bh) * 256 + threadIdx.x;
-  float S = p.h0 ? p.h0[bh * PN + e] : 0.f;
+  const int64_t e = (blockIdx.x % blocks_per_bh) * 256 + threadIdx.x;  // record order
+  float S = 0.f;
+  if (p.h0) {
+    int row, col;
+    rec_element<N, WM>((uint32_t)e, row, col);
+    S = p.h0[bh * PN + row * N + col];
+  }
   const int64_t ng1 = p.ngroups - 1;
   for (int64_t jj = 0; jj < ng1; ++jj) {
     const int64_t slot = bh * ng1 + jj;
@@ -775,8 +817,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
         const int64_t i = (i0 + q < j) ? i0 + q : j - 1;
 #pragma unroll
         for (int t = 0; t < NN; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[q][t][r] = agg[i * (kP * N) + SS::row(r) * N + SS::col(t)];
+          v[q][t] = *reinterpret_cast<const f32x4 *>(agg + i * (kP * N) + (t * T + threadIdx.x) * 4);
       }
 #pragma unroll
       for (int q = 0; q < R; ++q) {
@@ -1101,11 +1142,9 @@ ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, con
     const int64_t g1 = 8 * ((t1 + 7) / 8);
     hipLaunchKernelGGL((ssd_group_state_kernel<Q, N, F32, IO>), dim3((unsigned)g1), dim3(256),
                        0, stream, prm);
-    if (prm.chained) {
-      const int PN = kP * N;
-      hipLaunchKernelGGL(ssd_group_passing_kernel, dim3((unsigned)(bh * (PN / 256))), dim3(256), 0,
-                         stream, prm, PN);
-    }
+    if (prm.chained)
+      hipLaunchKernelGGL((ssd_group_passing_kernel<N, main_waves<Q>()>),
+                         dim3((unsigned)(bh * (kP * N / 256))), dim3(256), 0, stream, prm);
   }
   const int64_t t2 = bh * pl.ngroups;
   const int64_t g2 = 8 * ((t2 + 7) / 8);
@@ -1113,7 +1152,7 @@ ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, con
     return SSD_ERR_LAUNCH;
   // 4-wave workgroups (two per CU) for chunks of 64 and 128 tokens; 8 waves
   // for 256-token chunks, whose row tiles would not fit 4 waves' registers
-  constexpr int W = Q == 256 ? 8 : 4;
+  constexpr int W = main_waves<Q>();
   if (prm.z)
     hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, F32, IO, W, true>), dim3((unsigned)g2),
                        dim3(64 * W), 0, stream, prm);
