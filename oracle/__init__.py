@@ -10,6 +10,8 @@ Contents
   forms      : two independent restatements used to pin the recurrence --
                the quadratic semiseparable-matrix form and the four-stage
                chunked form -- plus the A = 0 closed form.
+  rmsnorm    : ``rmsnorm_gated`` -- the gated grouped RMSNorm that follows
+               chunk_scan in the chain (fp64 NumPy).
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``
 (hand-derived golden values, closed forms, cross-form equality and
@@ -18,3 +20,4 @@ invariants); none is "parity unpinned".
 from .recurrence import ssd_recurrence, build_oracle, oracle_max_threads  # noqa: F401
 from .forms import (ssd_quadratic, ssd_chunked, ssd_linear_attention_closed_form,  # noqa: F401
                     discretize)
+from .rmsnorm import rmsnorm_gated  # noqa: F401
