@@ -11,6 +11,10 @@ Prints ONE JSON line: whole-step throughput (tokens/s), plus
                   with HIP events recorded around its launch in every timed
                   step; achieved = algorithmic bytes / its mean duration;
   cpu_baseline -- the fp64 oracle on this host's cores over a bounded sample.
+
+``--op rmsnorm_gated`` instead times the gated grouped RMSNorm that follows
+the SSD forward (page "ops-transformer MambaV2 算子套件", section 4.6) on the
+configuration's output shape [B*L, H*P] with G groups: a step is one launch.
 """
 from __future__ import annotations
 
@@ -24,10 +28,11 @@ import time
 
 import torch
 
-from workloads import WORKLOADS, Workload, make_inputs
+from workloads import NORM_EPS, WORKLOADS, Workload, make_inputs, norm_inputs, norm_shape
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "SSD fwd ms & tokens/s at [B,L,H,P,N,chunk,G]; % of MFMA/HBM roofline"
+NORM_METRIC = "gated RMSNorm ms & tokens/s at [B*L, H*P], G groups; % of HBM roofline"
 # Published figure for [4,2048,16,64,128,128,4]: 0.632 ms on Ascend 910B3
 # (page "Mamba-2 SSD for Ascend NPU", Benchmark table) = 4*2048/0.632e-3 tokens/s.
 PAGE_TOKENS_PER_S = {"same_device": 4 * 2048 / 0.632e-3,
@@ -56,13 +61,15 @@ def algorithmic_flops(w: Workload) -> int:
     return 2 * w.batch * nc * (G * Q * Q * N + H * Q * Q * P + 2 * H * Q * N * P)
 
 
-def measured_traffic(w: Workload):
-    """HBM bytes per main-kernel launch measured with rocprofv3 counters
-    (FETCH_SIZE + WRITE_SIZE, copy-calibrated; profiles/traffic.json), or
-    None when the kernel source changed since the counters were taken."""
+def measured_traffic(name: str, kernel: str = "ssd_chunk_scan_kernel",
+                     record: str = "traffic.json"):
+    """HBM bytes per launch of ``kernel`` on workload ``name``, measured with
+    rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, copy-calibrated; a record
+    under profiles/), or None when the kernel source changed since the
+    counters were taken."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", "traffic.json")
+    path = os.path.join(here, "profiles", record)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -73,7 +80,7 @@ def measured_traffic(w: Workload):
     with open(src, "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != rec.get("kernel_source_sha256"):
             return None
-    k = rec.get("workloads", {}).get(w.name, {}).get("ssd_chunk_scan_kernel")
+    k = rec.get("workloads", {}).get(name, {}).get(kernel)
     return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
 
 
@@ -87,6 +94,7 @@ class HipEvents:
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self) -> ctypes.c_void_p:
         ev = ctypes.c_void_p()
@@ -101,6 +109,11 @@ class HipEvents:
         if rc != 0:
             raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
         return float(ms.value)
+
+    def record(self, ev, stream: int):
+        rc = self.hip.hipEventRecord(ev, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
 
     def destroy(self, ev):
         self.hip.hipEventDestroy(ev)
@@ -163,12 +176,123 @@ def cpu_baseline(w: Workload, budget_s: float):
                       f"threads; scaled to the whole workload"}
 
 
+def copy_calibration(mb: int, dev: str) -> None:
+    """A plain device copy of known size, run three times: the reference
+    kernel that scales the HBM byte counters."""
+    if mb <= 0:
+        return
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {n * 4} bytes read + {n * 4} written per copy",
+          file=sys.stderr, flush=True)
+    del src, dst
+
+
+def norm_bytes(rows: int, dim: int, gate: bool = True) -> int:
+    """x, z and out once each, plus the weight."""
+    return (3 if gate else 2) * 4 * rows * dim + 4 * dim
+
+
+def norm_cpu_baseline(rows: int, dim: int, G: int, seed: int, budget_s: float):
+    """The fp64 norm oracle on a bounded sample of rows, scaled to tokens/s."""
+    from oracle import rmsnorm_gated as oracle_norm
+    n = min(rows, 256)
+    d = norm_inputs(n, dim, seed)
+    x, z, wt = d["x"].numpy(), d["z"].numpy(), d["w"].numpy()
+    reps, t = 0, 0.0
+    while t < budget_s:
+        t0 = time.perf_counter()
+        oracle_norm(x, z, wt, G, NORM_EPS)
+        t += time.perf_counter() - t0
+        reps += 1
+    return {"value": n * reps / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} rows of [{rows}, {dim}] (G={G}), {reps} repetition(s), {t:.1f} s of "
+                      f"fp64 numpy on one thread; tokens/s = rows/s"}
+
+
+def norm_main(args, w: Workload) -> int:
+    import mamba_ssd_chunked_04_amd as ssd
+    rows, dim, G = norm_shape(w)
+    dev = "cuda:0"
+    abytes = norm_bytes(rows, dim)
+    n_sets = args.sets or max(1, min(16, math.ceil(2 * 512e6 / abytes)))
+    print(f"[bench] gated RMSNorm after {w.name}: rows={rows} dim={dim} G={G} sets={n_sets}",
+          file=sys.stderr, flush=True)
+    sets = []
+    for k in range(n_sets):
+        d = norm_inputs(rows, dim, w.seed * 1000 + 500 + k, device=dev)
+        d["out"] = torch.empty_like(d["x"])
+        sets.append(d)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+
+    copy_calibration(args.copy_calibration_mb, dev)
+
+    def step(k):
+        d = sets[k % n_sets]
+        ssd.rmsnorm_gated(d["x"], d["z"], d["w"], G, NORM_EPS, out=d["out"])
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    # A step is one launch, so the kernel's mean duration is taken over the
+    # back-to-back launches between two events (an event pair around each
+    # launch of a ~17 us kernel would add its own ~3 us to every sample).
+    K = args.steps
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.record(e0, stream)
+    for k in range(K):
+        step(k)
+    ev.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kmean = ev.elapsed_ms(e0, e1) / K
+    ev.destroy(e0)
+    ev.destroy(e1)
+    achieved = abytes / (kmean * 1e-3) / 1e9
+    rec = {
+        "metric": NORM_METRIC,
+        "value": rows / (wall / K),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"gated RMSNorm after {w.name} {w.shape_str()}", "rows": rows,
+                   "dim": dim, "G": G, "group_size": dim // G, "eps": NORM_EPS, "z": True,
+                   "input_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name, "gated_rmsnorm_kernel",
+                                                 "traffic_rmsnorm.json"),
+                     "kernel": "gated_rmsnorm_kernel", "kernel_ms": kmean,
+                     "algorithmic_bytes": abytes},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = norm_cpu_baseline(rows, dim, G, w.seed, args.cpu_baseline_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="same_device", choices=sorted(WORKLOADS))
+    ap.add_argument("--op", default="ssd_fwd", choices=["ssd_fwd", "rmsnorm_gated"])
     ap.add_argument("--mma", default="f16", choices=["f16", "f32"])
     ap.add_argument("--chunks-per-wg", type=int, default=0)
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = auto)")
@@ -192,6 +316,8 @@ def main(argv=None):
     w = WORKLOADS[args.config]
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.op == "rmsnorm_gated":
+        return norm_main(args, w)
     print(f"[bench] workload {w.name} {w.shape_str()} mma={args.mma}", file=sys.stderr, flush=True)
 
     # rotating input/output sets: total footprint > 2 x 256 MB Infinity Cache
@@ -211,16 +337,7 @@ def main(argv=None):
     cpg, ngroups = ssd.plan(calls[0].desc, w.chunk)
     stream = torch.cuda.current_stream().cuda_stream
 
-    if args.copy_calibration_mb > 0:
-        n = args.copy_calibration_mb * (1 << 20) // 4
-        src = torch.ones(n, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copy calibration: {n * 4} bytes read + {n * 4} written per copy",
-              file=sys.stderr, flush=True)
-        del src, dst
+    copy_calibration(args.copy_calibration_mb, dev)
 
     for k in range(args.warmup):
         calls[k % n_sets].launch(stream)
@@ -267,7 +384,7 @@ def main(argv=None):
                    "initial_state": w.has_h0, "final_state": True,
                    "chunks_per_wg": cpg, "chunk_groups": ngroups, "input_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "kernel": "ssd_chunk_scan_kernel", "kernel_ms": main_mean,
                      "algorithmic_bytes": abytes},
         "path": {"ms": ms_per_step, "gbs": abytes / (wall / K) / 1e9,

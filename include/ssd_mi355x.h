@@ -129,6 +129,26 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A,
                    void *out, float *final_state, void *stream,
                    const ssd_desc *d);
 
+/* Gated grouped RMSNorm, the operator that closes the SSD chain (page
+ * "ops-transformer MambaV2 算子套件", §4.6, mamba2_rmsnormgated):
+ *
+ *   g   = x * silu(z)                  (g = x when z is NULL)
+ *   out = g / sqrt(mean(g^2 over its group) + eps) * w
+ *
+ * where each row of `dim` elements splits into `ngroups` contiguous groups
+ * of dim/ngroups elements, and silu(v) = v / (1 + exp(-v)).
+ *   x, z, out  [rows, dim]  fp32     w [dim] fp32     eps >= 0, finite
+ * rows is any product of leading dimensions (B*S for the page's [B,S,D]).
+ * out may be x or z itself (in-place); w must not overlap out.  Errors:
+ * SSD_ERR_INVALID_ARG for a NULL x/w/out, rows/dim/ngroups < 1, ngroups not
+ * dividing dim, a negative or non-finite eps or a pointer not 16-byte
+ * aligned; SSD_ERR_UNSUPPORTED when dim/ngroups is not a multiple of 4 or
+ * above 4096, rows*dim reaches 2^40 elements or ceil(rows/4)*ngroups
+ * reaches 2^31 (one workgroup per four rows of one group). */
+ssd_status ssd_rmsnorm_gated(const float *x, const float *z, const float *w,
+                             int64_t rows, int64_t dim, int64_t ngroups,
+                             float eps, float *out, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *ssd_status_str(int status);
 

@@ -19,7 +19,7 @@ SSD_MMA_F16, SSD_MMA_F32 = 0, 2
 
 # Every symbol include/ssd_mi355x.h declares.
 EXPORTED_SYMBOLS = ("ssd_desc_init", "ssd_fwd_workspace_size", "ssd_fwd_plan", "ssd_fwd",
-                    "ssd_status_str", "ssd_abi_version")
+                    "ssd_rmsnorm_gated", "ssd_status_str", "ssd_abi_version")
 
 
 class SsdDesc(ctypes.Structure):
@@ -66,6 +66,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ssd_fwd_plan.restype = c_int
     lib.ssd_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, c_int, c_int, vp, vp, vp, dp]
     lib.ssd_fwd.restype = c_int
+    lib.ssd_rmsnorm_gated.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_float, vp, vp]
+    lib.ssd_rmsnorm_gated.restype = c_int
     lib.ssd_status_str.argtypes = [c_int]
     lib.ssd_status_str.restype = ctypes.c_char_p
     lib.ssd_abi_version.argtypes = []
@@ -214,3 +216,34 @@ def ssd_fwd(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     with torch.cuda.device(x.device):
         call.launch(torch.cuda.current_stream(x.device).cuda_stream)
     return (out, fin) if return_final_state else out
+
+
+def rmsnorm_gated(x, z, weight, ngroups: int, eps: float = 1e-5, out=None):
+    """Gated grouped RMSNorm over the last dimension on the current torch stream.
+
+    x, z: [..., D] float32 GPU tensors (z may be None: no gate); weight: [D].
+    Returns ``out`` (allocated unless given; it may be ``x`` for in-place).
+    """
+    import torch
+    for name, t in (("x", x), ("weight", weight)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    D = x.shape[-1]
+    if weight.shape != (D,) or (z is not None and z.shape != x.shape):
+        raise ValueError("shape mismatch: x[..., D], z like x, weight[D]")
+    if out is None:
+        out = torch.empty_like(x)
+    for t in (x, z, weight, out):
+        if t is None:
+            continue
+        if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous():
+            raise ValueError("x, z, weight and out must be contiguous float32 on one GPU")
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    rows = x.numel() // D if D else 0
+    with torch.cuda.device(x.device):
+        st = torch.cuda.current_stream(x.device).cuda_stream
+        _raise_for(load_library().ssd_rmsnorm_gated(_ptr(x), _ptr(z), _ptr(weight), rows, D,
+                                                    int(ngroups), float(eps), _ptr(out),
+                                                    ctypes.c_void_p(st)), "ssd_rmsnorm_gated")
+    return out

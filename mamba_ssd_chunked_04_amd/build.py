@@ -1,7 +1,7 @@
 """Compile the HIP library for gfx950, in-tree.
 
-Produces mamba_ssd_chunked_04_amd/libssd_mi355x.so from csrc/ssd_fwd.hip with
-hipcc.  Packed-fp32 instruction selection is switched off for all device
+Produces mamba_ssd_chunked_04_amd/libssd_mi355x.so from the HIP sources in
+csrc/ (the SSD forward and the gated RMSNorm) with hipcc.  Packed-fp32 instruction selection is switched off for all device
 code (-Xclang -target-feature -Xclang -packed-fp32-ops).
 """
 from __future__ import annotations
@@ -13,7 +13,7 @@ import time
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
-SRC = os.path.join(PKG_DIR, "csrc", "ssd_fwd.hip")
+SRCS = tuple(os.path.join(PKG_DIR, "csrc", f) for f in ("ssd_fwd.hip", "rmsnorm_gated.hip"))
 HEADER = os.path.join(REPO_DIR, "include", "ssd_mi355x.h")
 LIB = os.path.join(PKG_DIR, "libssd_mi355x.so")
 ARCH = "gfx950"
@@ -23,7 +23,7 @@ def hipcc_command(out_path: str = LIB, extra=()) -> list:
     hipcc = os.environ.get("HIPCC", "hipcc")
     return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-pass-failed", "-I", os.path.join(REPO_DIR, "include"), SRC, "-o", out_path, *extra]
+            "-Wno-pass-failed", "-I", os.path.join(REPO_DIR, "include"), *SRCS, "-o", out_path, *extra]
 
 
 def build_library(verbose: bool = True) -> str:
@@ -49,7 +49,7 @@ def library_is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(f) > t for f in (SRC, HEADER))
+    return any(os.path.getmtime(f) > t for f in (*SRCS, HEADER))
 
 
 if __name__ == "__main__":

@@ -168,6 +168,36 @@ def test_workload_plans(lib, name):
     assert ssd.plan(d, w.chunk) == (1, nc)
 
 
+def _rms(lib, x=FAKE, z=None, w=FAKE, rows=8, dim=256, ngroups=1, eps=1e-5, out=FAKE):
+    return lib.ssd_rmsnorm_gated(x, z, w, rows, dim, ngroups, eps, out, None)
+
+
+@pytest.mark.parametrize("kw", [dict(x=None), dict(w=None), dict(out=None), dict(rows=0),
+                                dict(dim=0), dict(ngroups=0), dict(dim=256, ngroups=3),
+                                dict(eps=-1e-6), dict(eps=float("nan")), dict(eps=float("inf")),
+                                dict(x=FAKE + 4), dict(z=FAKE + 8), dict(w=FAKE + 12),
+                                dict(out=FAKE + 4)],
+                         ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_rmsnorm_invalid_args(lib, kw):
+    assert _rms(lib, **kw) == bnd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(dim=6, ngroups=1),            # group size not a multiple of 4
+                                dict(dim=8200, ngroups=2),         # group size 4100 > 4096
+                                dict(rows=1 << 24, dim=2048, ngroups=512),  # 2^31 blocks
+                                dict(rows=1 << 31, dim=1024)],     # 2^41 elements
+                         ids=["gsz6", "gsz4100", "blocks2^31", "rows2^31"])
+def test_rmsnorm_unsupported(lib, kw):
+    assert _rms(lib, **kw) == bnd.SSD_ERR_UNSUPPORTED
+
+
+def test_rmsnorm_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 8)
+    with pytest.raises(ValueError):
+        ssd.rmsnorm_gated(x, None, torch.ones(8), 2)
+
+
 def test_product_path_does_not_touch_oracle():
     """The HIP path and its binding never import or load the oracle."""
     pkg = os.path.join(ROOT, "mamba_ssd_chunked_04_amd")

@@ -108,3 +108,33 @@ def random_inputs(Bsz: int, L: int, H: int, P: int, N: int, G: int, seed: int,
     else:
         d["dt_bias"] = None
     return d
+
+
+# ------------------------------------------------------------------ gated RMSNorm
+# The norm that closes the SSD chain (page "ops-transformer MambaV2 算子套件",
+# section 4.6) runs on out[B, S, D] with D = H * P, in G contiguous groups.
+# Its workload for an SSD workload w is [w.batch, w.seqlen, w.nheads*w.headdim]
+# with G = w.ngroups.  x stands in for the SSD output and z for the gate,
+# both ~ N(0,1); the weight is 1 + 0.1 * N(0,1) (an RMSNorm weight near its
+# initial value of one; the page gives no distribution); eps = 1e-5.
+NORM_EPS = 1e-5
+
+
+def norm_shape(w: Workload):
+    """(rows, dim, ngroups) of the norm that follows workload ``w``."""
+    return w.batch * w.seqlen, w.nheads * w.headdim, w.ngroups
+
+
+def norm_inputs(rows: int, dim: int, seed: int, has_z: bool = True,
+                device: str = "cpu") -> Dict[str, Optional[torch.Tensor]]:
+    """x [rows, dim], z [rows, dim] (or None), w [dim], all fp32, drawn in the
+    order x, z, w from a generator on ``device`` (CPU bits are reproducible
+    everywhere; a GPU generator is used for inputs too large to draw on the
+    host, and only its own draws are compared)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    f32 = torch.float32
+    x = torch.randn(rows, dim, generator=g, device=device, dtype=f32)
+    z = torch.randn(rows, dim, generator=g, device=device, dtype=f32) if has_z else None
+    wt = 1.0 + 0.1 * torch.randn(dim, generator=g, device=device, dtype=f32)
+    return {"x": x, "z": z, "w": wt}
