@@ -12,8 +12,12 @@ Contents
                chunked form -- plus the A = 0 closed form.
   rmsnorm    : ``rmsnorm_gated`` -- the gated grouped RMSNorm that follows
                chunk_scan in the chain (fp64 NumPy).
+  varlen     : ``ssd_varlen`` -- packed variable-length sequences (state reset
+               at each cu_seqlens start), the recurrence per sequence, and
+               ``ssd_quadratic_seq_idx``, the same as one masked matrix.
 
-Parity status: every function here is pinned by ``tests/test_oracle.py``
+Parity status: every function here is pinned by ``tests/test_oracle.py``,
+``tests/test_oracle_rmsnorm.py`` or ``tests/test_oracle_varlen.py``
 (hand-derived golden values, closed forms, cross-form equality and
 invariants); none is "parity unpinned".
 """
@@ -21,3 +25,4 @@ from .recurrence import ssd_recurrence, build_oracle, oracle_max_threads  # noqa
 from .forms import (ssd_quadratic, ssd_chunked, ssd_linear_attention_closed_form,  # noqa: F401
                     discretize)
 from .rmsnorm import rmsnorm_gated  # noqa: F401
+from .varlen import ssd_quadratic_seq_idx, ssd_varlen  # noqa: F401
