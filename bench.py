@@ -50,7 +50,8 @@ def algorithmic_bytes(w: Workload, ret_final: bool = True) -> int:
     b += 2 * T * G * N * s_io                # B, C
     b += 4 * T * H                           # dt
     b += 4 * H * (1 + (1 if w.has_D else 0))  # A, D
-    b += 4 * w.batch * H * P * N * ((1 if ret_final else 0) + (1 if w.has_h0 else 0))
+    b += 4 * w.nseq * H * P * N * ((1 if ret_final else 0) + (1 if w.has_h0 else 0))
+    b += 4 * (w.nseq + 1) if w.packed else 0  # cu_seqlens
     return b
 
 
@@ -133,8 +134,10 @@ def gpu_input_set(w: Workload, seed: int, device: str):
          "C": torch.randn(Bsz, L, G, N, generator=g, device=device, dtype=f32).to(io)}
     d["D"] = torch.randn(H, generator=g, device=device, dtype=f32) if w.has_D else None
     d["z"] = torch.randn(Bsz, L, H, P, generator=g, device=device, dtype=f32) if w.has_z else None
-    d["initial_states"] = (0.1 * torch.randn(Bsz, H, P, N, generator=g, device=device, dtype=f32)
+    d["initial_states"] = (0.1 * torch.randn(w.nseq, H, P, N, generator=g, device=device, dtype=f32)
                            if w.has_h0 else None)
+    if w.packed:
+        d["cu_seqlens"] = w.cu_seqlens().to(device)
     return d
 
 
@@ -144,6 +147,8 @@ def cpu_baseline(w: Workload, budget_s: float):
     ``budget_s`` seconds of CPU work, scaled to tokens/s of the workload."""
     from oracle import oracle_max_threads, ssd_recurrence
     d = make_inputs(w)
+    if w.packed:
+        return packed_cpu_baseline(w, d, budget_s, oracle_max_threads())
     BH = w.batch * w.nheads
     all_pairs = [(b, h) for b in range(w.batch) for h in range(w.nheads)]
     threads = oracle_max_threads()
@@ -286,6 +291,22 @@ def norm_main(args, w: Workload) -> int:
     return 0
 
 
+def packed_cpu_baseline(w: Workload, d, budget_s: float, threads: int):
+    """The fp64 packed oracle (each sequence through the recurrence) over the
+    whole packed workload, repeated to about ``budget_s`` seconds."""
+    from oracle import ssd_varlen
+    reps, t = 0, 0.0
+    while t < budget_s:
+        t0 = time.perf_counter()
+        ssd_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["cu_seqlens"], D=d["D"], z=d["z"],
+                   initial_states=d["initial_states"], dt_softplus=True)
+        t += time.perf_counter() - t0
+        reps += 1
+    return {"value": w.tokens * reps / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole packed {w.shape_str()} workload ({w.nseq} sequences), {reps} "
+                      f"repetition(s), {t:.1f} s of fp64 recurrence on {threads} OpenMP threads"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,7 +353,9 @@ def main(argv=None):
         call, out, fin, wsp = ssd.prepare(d["x"], d["dt"], d["A"], d["B"], d["C"], w.chunk,
                                           D=d["D"], z=d["z"], initial_states=d["initial_states"],
                                           dt_softplus=True, return_final_state=True, mma=args.mma,
-                                          chunks_per_wg=args.chunks_per_wg)
+                                          chunks_per_wg=args.chunks_per_wg,
+                                          cu_seqlens=d.get("cu_seqlens"),
+                                          max_seqlen=w.max_len if w.packed else None)
         calls.append(call)
     cpg, ngroups = ssd.plan(calls[0].desc, w.chunk)
     stream = torch.cuda.current_stream().cuda_stream
@@ -382,6 +405,7 @@ def main(argv=None):
                    "H": w.nheads, "P": w.headdim, "N": w.dstate, "chunk": w.chunk,
                    "G": w.ngroups, "io_dtype": w.io_dtype, "D": w.has_D, "z": w.has_z,
                    "initial_state": w.has_h0, "final_state": True,
+                   "seqlens": list(w.seqlens) if w.packed else None,
                    "chunks_per_wg": cpg, "chunk_groups": ngroups, "input_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),

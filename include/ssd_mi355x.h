@@ -40,8 +40,9 @@ extern "C" {
 typedef enum {
   SSD_OK = 0,
   SSD_ERR_INVALID_ARG = 1,  /* NULL required pointer, dim < 1, H % G != 0,
-                               misaligned pointer, bad dtype/mma code,
-                               final_state NULL while requested       */
+                               misaligned pointer (cu_seqlens: 4 bytes),
+                               bad dtype/mma code, final_state NULL
+                               while requested                        */
   SSD_ERR_UNSUPPORTED = 2,  /* valid but not compiled: headdim != 64,
                                dstate not in {64,128}, chunk not in
                                {64,128,256}, fp16 storage, or one batch
@@ -93,6 +94,32 @@ typedef struct ssd_desc {
                                 stream right before the main-pass kernel, for
                                 measurement; NULL records nothing             */
   void *ev_main_end;         /* optional hipEvent_t recorded right after it   */
+  const int32_t *cu_seqlens; /* packed variable-length sequences, or NULL.
+                                When set, `batch` sequences of different
+                                lengths share one token axis: x, z, out are
+                                [T,H,P], dt [T,H], B and C [T,G,N], where
+                                sequence s holds tokens cu_seqlens[s] ..
+                                cu_seqlens[s+1]-1 (DEVICE array of batch+1
+                                int32, cu_seqlens[0] = 0, non-decreasing,
+                                T = cu_seqlens[batch]).  The state starts
+                                from initial_state[s] (or zero) at each
+                                sequence and final_state[s] is the state
+                                after its last token; initial_state and
+                                final_state stay [batch,H,P,N].  `seqlen`
+                                is then the longest sequence: the plan is
+                                made for it, and a longer sequence is
+                                processed only up to `seqlen` tokens (the
+                                out rows past that are not written).
+                                Readings of page "Mamba-2 SSD for Ascend
+                                NPU", "Limitations and roadmap" (varlen,
+                                cu_seqlens) and page "ops-transformer
+                                MambaV2 算子套件" §1.4 (packed batches
+                                delimited by cumulative offsets)          */
+  int64_t packed_tokens;     /* with cu_seqlens: T, the packed token count
+                                (cu_seqlens[batch]), which the plan uses to
+                                spread the work of uneven lengths; 0 plans
+                                as if every sequence had `seqlen` tokens.
+                                Ignored for dense calls                   */
 } ssd_desc;
 
 /* Fills `d` with defaults for the given shape: fp32 storage, fp16 MMA, no
@@ -155,7 +182,7 @@ const char *ssd_status_str(int status);
 /* ABI version of this header (bumped on any incompatible change). */
 int ssd_abi_version(void);
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

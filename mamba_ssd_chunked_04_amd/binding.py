@@ -34,6 +34,7 @@ class SsdDesc(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("chunks_per_wg", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p), ("packed_tokens", ctypes.c_int64),
     ]
 
 
@@ -144,11 +145,18 @@ class SsdCall:
 def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initial_states=None,
             dt_softplus: bool = False, dt_limit: Tuple[float, float] = (0.0, math.inf),
             return_final_state: bool = False, mma: str = "f16", out_dtype=None,
-            chunks_per_wg: int = 0, out=None, final_state=None, workspace=None):
+            chunks_per_wg: int = 0, out=None, final_state=None, workspace=None,
+            cu_seqlens=None, max_seqlen: Optional[int] = None):
     """Validate torch tensors, allocate outputs/workspace, and build an SsdCall.
 
     ``out`` is float32 unless ``out_dtype`` (float32 or bfloat16) says
     otherwise, whatever the dtype of x, B and C.
+
+    Packed variable-length sequences: x [1, T, H, P] (dt [1, T, H], B/C
+    [1, T, G, N], z like x) with ``cu_seqlens`` an int32 GPU tensor of
+    nseq+1 token offsets; initial and final states are then [nseq, H, P, N].
+    ``max_seqlen`` (the longest sequence) is read from cu_seqlens when not
+    given, which synchronises with the device.
     Returns (call, out, final_state_or_None, workspace_or_None).
     """
     import torch
@@ -158,6 +166,19 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     dev = x.device
     Bsz, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
+    nrows, row_len = Bsz, L                     # batch rows of the call and their length
+    if cu_seqlens is not None:
+        if Bsz != 1:
+            raise ValueError("packed sequences take x of shape [1, T, H, P]")
+        if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.device != dev
+                or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+                or cu_seqlens.numel() < 2 or not cu_seqlens.is_contiguous()):
+            raise ValueError("cu_seqlens must be a contiguous int32 tensor of nseq+1 offsets "
+                             "on the GPU of x")
+        nrows = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
+        row_len = max(1, int(max_seqlen))
     if dt.shape != (Bsz, L, H) or A.shape != (H,) or B.shape != (Bsz, L, G, N) or C.shape != B.shape:
         raise ValueError("shape mismatch: x[B,L,H,P], dt[B,L,H], A[H], B/C[B,L,G,N]")
     if B.dtype != x.dtype or C.dtype != x.dtype:
@@ -167,7 +188,7 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
         if t is not None and t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32")
     opt_shapes = (("D", D, (H,)), ("dt_bias", dt_bias, (H,)), ("z", z, (Bsz, L, H, P)),
-                  ("initial_states", initial_states, (Bsz, H, P, N)))
+                  ("initial_states", initial_states, (nrows, H, P, N)))
     for name, t, shp in opt_shapes:
         if t is not None and tuple(t.shape) != shp:
             raise ValueError(f"{name} must have shape {shp}")
@@ -179,8 +200,11 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     if out is None:
         out = torch.empty(Bsz, L, H, P, device=dev, dtype=out_dtype)
     if return_final_state and final_state is None:
-        final_state = torch.empty(Bsz, H, P, N, device=dev, dtype=torch.float32)
-    desc = make_desc(Bsz, L, H, P, N, G)
+        final_state = torch.empty(nrows, H, P, N, device=dev, dtype=torch.float32)
+    desc = make_desc(nrows, row_len, H, P, N, G)
+    if cu_seqlens is not None:
+        desc.cu_seqlens = cu_seqlens.data_ptr()
+        desc.packed_tokens = L
     desc.x_dtype = _dtype_code(x.dtype)
     desc.z_dtype = _dtype_code(z.dtype) if z is not None else SSD_F32
     desc.out_dtype = _dtype_code(out.dtype)
@@ -196,23 +220,26 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk_size),
             int(bool(dt_softplus)), int(bool(return_final_state)), _ptr(out),
             _ptr(final_state) if return_final_state else None)
-    keep = (x, dt, A, B, C, D, z, dt_bias, initial_states, out, final_state, workspace)
+    keep = (x, dt, A, B, C, D, z, dt_bias, initial_states, out, final_state, workspace, cu_seqlens)
     return SsdCall(args, desc, keep), out, (final_state if return_final_state else None), workspace
 
 
 def ssd_fwd(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initial_states=None,
             dt_softplus: bool = False, dt_limit: Tuple[float, float] = (0.0, math.inf),
             return_final_state: bool = False, mma: str = "f16", out_dtype=None,
-            chunks_per_wg: int = 0):
+            chunks_per_wg: int = 0, cu_seqlens=None, max_seqlen: Optional[int] = None):
     """SSD chunked forward on the current torch stream.
 
     Returns ``out`` or ``(out, final_state)`` when ``return_final_state``.
+    With ``cu_seqlens`` the call runs packed variable-length sequences (see
+    ``prepare``).
     """
     import torch
     call, out, fin, _ws = prepare(x, dt, A, B, C, chunk_size, D=D, z=z, dt_bias=dt_bias,
                                   initial_states=initial_states, dt_softplus=dt_softplus,
                                   dt_limit=dt_limit, return_final_state=return_final_state,
-                                  mma=mma, out_dtype=out_dtype, chunks_per_wg=chunks_per_wg)
+                                  mma=mma, out_dtype=out_dtype, chunks_per_wg=chunks_per_wg,
+                                  cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
     with torch.cuda.device(x.device):
         call.launch(torch.cuda.current_stream(x.device).cuda_stream)
     return (out, fin) if return_final_state else out

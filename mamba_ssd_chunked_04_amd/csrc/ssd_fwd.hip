@@ -28,7 +28,11 @@
 //   * the masked C.B^T block is computed transposed, so its accumulator
 //     layout is directly the A operand of the M.X product (no LDS round trip);
 //   * workgroup ids are swizzled so heads sharing a B/C group run on the same
-//     XCD (shared L2).
+//     XCD (shared L2);
+//   * packed variable-length sequences (cu_seqlens) are batch rows whose
+//     token span comes from the offsets: each is chunked from its own start
+//     and its state restarts there, the form page "Mamba-2 SSD for Ascend
+//     NPU" lists under "Limitations and roadmap" (varlen, cu_seqlens).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -168,25 +172,37 @@ struct Params {
   float *grp_state;  // [B*H][ngroups-1][P*N]: group aggregates (state from a zero
                      // start), or entering states once the passing pass ran
   float *grp_lam;    // [B*H][ngroups-1]: group total log2-decay
+  const int32_t *cu_seqlens;  // packed calls: [batch+1] token offsets, else NULL
   int64_t batch, L, H, G, nc, ngroups, cpg;
+  int Q;
   float dt_min, dt_max;
   int dt_softplus, z_bf16, out_bf16, ret_final;
   int chained;  // grp_state holds entering states (the passing pass ran)
 };
 
 // Workgroup id -> (b, h, chunk group).  Tiles are ordered (b, group, g, head
-// in group) and dealt in contiguous runs to the 8 XCDs (workgroup n runs on
-// XCD n % 8), so the heads that share one B/C group run side by side on one
-// XCD and share its L2.  With `late_first` the chunk groups are dealt from
-// the last one down (later groups have more to do before their first chunk).
+// in group); workgroup n runs on XCD n % 8.  Dense calls deal the tiles in
+// contiguous runs to the XCDs, so the heads that share one B/C group run side
+// by side on one XCD and share its L2.  Packed calls, whose rows differ in
+// length, deal units of those heads round-robin over the XCDs instead (unit
+// u on XCD u % 8), so long and short sequences spread over all of them; the
+// grid then has 8 * hpg * ceil(units / 8) workgroups (tile_grid).  With
+// `late_first` the chunk groups are dealt from the last one down (later
+// groups have more to do before their first chunk).
 __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_here, int64_t &b,
                                             int64_t &h, int64_t &j, bool late_first = false) {
   const int64_t total = p.batch * p.H * ngroups_here;
   const int64_t n = blockIdx.x;
-  const int64_t per = (total + 7) / 8;
-  const int64_t T = (n % 8) * per + n / 8;
-  if (T >= total) return false;
   const int64_t hpg = p.H / p.G;
+  int64_t T;
+  if (p.cu_seqlens) {
+    const int64_t k = n / 8;
+    T = ((k / hpg) * 8 + n % 8) * hpg + k % hpg;
+  } else {
+    const int64_t per = (total + 7) / 8;
+    T = (n % 8) * per + n / 8;
+  }
+  if (T >= total) return false;
   const int64_t hh = T % hpg;
   int64_t rest = T / hpg;
   const int64_t g = rest % p.G;
@@ -198,21 +214,47 @@ __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_her
   return true;
 }
 
+// Tokens of batch row b: [start, start + len) on the token axis.  Dense
+// calls: b*L and L.  Packed calls: the row is sequence b of cu_seqlens, its
+// length clamped to [0, L] (L is then the longest sequence, which the plan
+// is made for).
+struct RowSpan {
+  int64_t start, len;
+};
+
+__device__ __forceinline__ RowSpan row_span(const Params &p, int64_t b) {
+  if (!p.cu_seqlens) return {b * p.L, p.L};
+  const int64_t s = p.cu_seqlens[b], e = p.cu_seqlens[b + 1];
+  const int64_t len = e - s;
+  return {s, len < 0 ? 0 : (len > p.L ? p.L : len)};
+}
+
+// Chunks of a row and the chunk groups that hold them; an empty row keeps
+// one group, which writes its final state (the initial state).
+__device__ __forceinline__ int64_t row_chunks(const Params &p, int64_t len) {
+  return (len + p.Q - 1) / p.Q;
+}
+__device__ __forceinline__ int64_t row_groups(const Params &p, int64_t len) {
+  const int64_t ng = (row_chunks(p, len) + p.cpg - 1) / p.cpg;
+  return ng < 1 ? 1 : ng;
+}
+
 // Buffer resources and element offsets of one (b, h) sequence.
 template <int N, class IO>
 struct SeqView {
   rsrc_t x, B, C;
   uint32_t H, G, h, g;
-  __device__ __forceinline__ SeqView(const Params &p, int64_t b, int64_t h_, int64_t g_) {
-    const uint64_t L = (uint64_t)p.L;
+  __device__ __forceinline__ SeqView(const Params &p, const RowSpan &rs, int64_t h_, int64_t g_) {
+    const uint64_t L = (uint64_t)rs.len, t0 = (uint64_t)rs.start;
     H = (uint32_t)p.H;
     G = (uint32_t)p.G;
     h = (uint32_t)h_;
     g = (uint32_t)g_;
     const uint64_t lhp = L * p.H * kP, lgn = L * p.G * N;
-    x = make_rsrc(static_cast<const char *>(p.x) + b * lhp * IO::esz, (uint32_t)(lhp * IO::esz));
-    B = make_rsrc(static_cast<const char *>(p.B) + b * lgn * IO::esz, (uint32_t)(lgn * IO::esz));
-    C = make_rsrc(static_cast<const char *>(p.C) + b * lgn * IO::esz, (uint32_t)(lgn * IO::esz));
+    const uint64_t ohp = t0 * p.H * kP, ogn = t0 * p.G * N;
+    x = make_rsrc(static_cast<const char *>(p.x) + ohp * IO::esz, (uint32_t)(lhp * IO::esz));
+    B = make_rsrc(static_cast<const char *>(p.B) + ogn * IO::esz, (uint32_t)(lgn * IO::esz));
+    C = make_rsrc(static_cast<const char *>(p.C) + ogn * IO::esz, (uint32_t)(lgn * IO::esz));
   }
   __device__ __forceinline__ uint32_t xoff(uint32_t t, uint32_t col) const { return (t * H + h) * kP + col; }
   __device__ __forceinline__ uint32_t boff(uint32_t t, uint32_t col) const { return (t * G + g) * N + col; }
@@ -289,7 +331,7 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
 // whether |delta*A| <= 7 (log2 units) for every token, which keeps the
 // factored intra-chunk decay of the main pass inside fp32 range.
 template <int Q>
-__device__ __forceinline__ void chunk_prep(const Params &p, uint32_t t0,
+__device__ __forceinline__ void chunk_prep(const Params &p, uint32_t t0, uint64_t len,
                                            float a_h, float bias, ChunkLds<Q> &cl, float &lend,
                                            bool &factored) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -300,7 +342,7 @@ __device__ __forceinline__ void chunk_prep(const Params &p, uint32_t t0,
   for (int m = 0; m < Q / 64; ++m) {
     float u = cl.dts[lane + 64 * m] + bias;
     if (p.dt_softplus) u = (u > 20.f) ? u : __logf(1.f + __expf(u));
-    const float delta = (t0 + lane + 64 * m < (uint64_t)p.L) ? fminf(fmaxf(u, p.dt_min), p.dt_max) : 0.f;
+    const float delta = (t0 + lane + 64 * m < len) ? fminf(fmaxf(u, p.dt_min), p.dt_max) : 0.f;
     const float a = delta * a_h * kLog2e;
     big |= fabsf(a) > 7.f;
     const float v = wave_inclusive_sum(a);
@@ -613,9 +655,11 @@ __global__ __launch_bounds__(256) void ssd_group_state_kernel(Params p) {
 
   int64_t b, h, j;
   if (!decode_tile(p, p.ngroups - 1, b, h, j)) return;
+  const RowSpan rs = row_span(p, b);
+  if (j >= row_groups(p, rs.len) - 1) return;  // the row's last group, or past its end
   const int64_t g = h / (p.H / p.G);
   const int64_t bh = b * p.H + h;
-  const SeqView<N, IO> sv(p, b, h, g);
+  const SeqView<N, IO> sv(p, rs, h, g);
 
   f32x4 sacc[NN];
 #pragma unroll
@@ -626,7 +670,7 @@ __global__ __launch_bounds__(256) void ssd_group_state_kernel(Params p) {
   const uint32_t tg = (uint32_t)(c_begin * Q);
   auto tok = [&](int i) { return tg + (uint32_t)(kJB * (i < nblk ? i : nblk - 1)); };
 
-  const rsrc_t rdt = make_rsrc(p.dt + b * p.L * p.H, (uint32_t)(p.L * p.H * 4));
+  const rsrc_t rdt = make_rsrc(p.dt + rs.start * p.H, (uint32_t)(rs.len * p.H * 4));
   const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
   // Each block buffer also carries the raw dt of the block one chunk later
   // (token 64 k + t of the group for block k + NB, thread t < 64; later
@@ -655,7 +699,7 @@ __global__ __launch_bounds__(256) void ssd_group_state_kernel(Params p) {
     ChunkLds<Q> &cl = clb[c & 1];
     if (jb == 0) {
       bool factored;
-      chunk_prep<Q>(p, (uint32_t)(c * Q), a_h, bias, cl, lend2, factored);
+      chunk_prep<Q>(p, (uint32_t)(c * Q), (uint64_t)rs.len, a_h, bias, cl, lend2, factored);
       const float dec = fast_exp2(lend2);
 #pragma unroll
       for (int t = 0; t < NN; ++t) sacc[t] *= dec;
@@ -712,7 +756,8 @@ __global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p) {
     S = p.h0[bh * PN + row * N + col];
   }
   const int64_t ng1 = p.ngroups - 1;
-  for (int64_t jj = 0; jj < ng1; ++jj) {
+  const int64_t ng1_row = row_groups(p, row_span(p, bh / p.H).len) - 1;  // filled slots
+  for (int64_t jj = 0; jj < ng1_row; ++jj) {
     const int64_t slot = bh * ng1 + jj;
     S = fast_exp2(p.grp_lam[slot]) * S + p.grp_state[slot * PN + e];
     p.grp_state[slot * PN + e] = S;
@@ -745,21 +790,24 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
 
   int64_t b, h, j;
   if (!decode_tile(p, p.ngroups, b, h, j, true)) return;
+  const RowSpan rs = row_span(p, b);
+  const int64_t ng_row = row_groups(p, rs.len), nc_row = row_chunks(p, rs.len);
+  if (j >= ng_row) return;  // past the end of a shorter packed sequence
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lq = lane >> 4;
   const int pt0 = RS::pt0(w);
   const int64_t g = h / (p.H / p.G);
-  const SeqView<N, IO> sv(p, b, h, g);
-  const uint64_t lhp = (uint64_t)p.L * p.H * kP;
+  const SeqView<N, IO> sv(p, rs, h, g);
+  const uint64_t lhp = (uint64_t)rs.len * p.H * kP, ohp = (uint64_t)rs.start * p.H * kP;
   const int osz = p.out_bf16 ? 2 : 4, zsz = p.z_bf16 ? 2 : 4;
-  const rsrc_t rout = make_rsrc(static_cast<char *>(p.out) + b * lhp * osz, (uint32_t)(lhp * osz));
-  const rsrc_t rz = make_rsrc(HAS_Z ? static_cast<const char *>(p.z) + b * lhp * zsz : nullptr,
+  const rsrc_t rout = make_rsrc(static_cast<char *>(p.out) + ohp * osz, (uint32_t)(lhp * osz));
+  const rsrc_t rz = make_rsrc(HAS_Z ? static_cast<const char *>(p.z) + ohp * zsz : nullptr,
                               HAS_Z ? (uint32_t)(lhp * zsz) : 0u);
   const bool z_bf16 = p.z_bf16 != 0;
   const float Dh = p.D ? p.D[h] : 0.f;
   const int64_t bh = b * p.H + h;
   const int64_t c_begin = j * p.cpg;
-  const int64_t c_end = (c_begin + p.cpg < p.nc) ? c_begin + p.cpg : p.nc;
-  auto qc_of = [&](int64_t c) { return (int)((p.L - c * Q) < Q ? (p.L - c * Q) : Q); };
+  const int64_t c_end = (c_begin + p.cpg < nc_row) ? c_begin + p.cpg : nc_row;
+  auto qc_of = [&](int64_t c) { return (int)((rs.len - c * Q) < Q ? (rs.len - c * Q) : Q); };
 
   // prefetch registers: next 64-token block (and its z), next chunk's C rows
   // and records
@@ -770,7 +818,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   };
   load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), nxt);
   load_zb((uint32_t)(c_begin * Q));
-  const rsrc_t rdt = make_rsrc(p.dt + b * p.L * p.H, (uint32_t)(p.L * p.H * 4));
+  const rsrc_t rdt = make_rsrc(p.dt + rs.start * p.H, (uint32_t)(rs.len * p.H * 4));
   const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
   // dt two chunks ahead in registers, one chunk ahead in LDS
   stage_dt<Q>(load_dt(rdt, sv.H, sv.h, (uint32_t)(c_begin * Q), Q), clb[c_begin & 1]);
@@ -841,7 +889,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
     if (!kPrefetchC) load_c(t0);
     float lend2;
     bool factored;
-    chunk_prep<Q>(p, t0, a_h, bias, cl, lend2, factored);
+    chunk_prep<Q>(p, t0, (uint64_t)rs.len, a_h, bias, cl, lend2, factored);
     lds_barrier();
     // chunk c-1's readers of the other buffer passed the barrier above
     stage_dt<Q>(dtr, clb[(c + 1) & 1]);
@@ -1040,7 +1088,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
       for (int r = 0; r < 4; ++r) sS[SS::row(r) * LDN + SS::col(t)] = (E)sacc[t][r];
   }
 
-  if (p.ret_final && j == p.ngroups - 1) {
+  if (p.ret_final && j == ng_row - 1) {
     float *dst = p.final_state + bh * (int64_t)(kP * N);
 #pragma unroll
     for (int t = 0; t < NN; ++t)
@@ -1083,7 +1131,7 @@ ssd_status check_shape(const ssd_desc *d, int64_t chunk) {
   if (d->out_dtype != SSD_F32 && d->out_dtype != SSD_BF16 && d->out_dtype != SSD_F16)
     return SSD_ERR_INVALID_ARG;
   if (d->mma != SSD_MMA_F16 && d->mma != SSD_MMA_F32) return SSD_ERR_INVALID_ARG;
-  if (d->chunks_per_wg < 0 || d->reserved != 0) return SSD_ERR_INVALID_ARG;
+  if (d->chunks_per_wg < 0 || d->reserved != 0 || d->packed_tokens < 0) return SSD_ERR_INVALID_ARG;
   if (!(d->dt_min <= d->dt_max)) return SSD_ERR_INVALID_ARG;  // also rejects NaN
   if (d->x_dtype == SSD_F16 || d->z_dtype == SSD_F16 || d->out_dtype == SSD_F16)
     return SSD_ERR_UNSUPPORTED;
@@ -1114,6 +1162,14 @@ Plan make_plan(const ssd_desc *d, int64_t chunk) {
   int64_t cpg;
   if (d->chunks_per_wg > 0) {
     cpg = d->chunks_per_wg;
+  } else if (d->cu_seqlens) {
+    // packed sequences: cut every sequence into groups of about the chunks
+    // per workgroup slot that the whole call needs (counting half a ragged
+    // chunk per sequence), so a long sequence among short ones does not walk
+    // all its chunks in one workgroup
+    const int64_t T = d->packed_tokens > 0 ? d->packed_tokens : d->batch * d->seqlen;
+    const int64_t chunks = (T + chunk - 1) / chunk + d->batch / 2;
+    cpg = chunks * d->nheads / target;
   } else if (bh >= target) {
     cpg = pl.nc;
   } else {
@@ -1134,20 +1190,30 @@ Plan make_plan(const ssd_desc *d, int64_t chunk) {
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 
+// Workgroups covering `ngroups_here` chunk groups of every (b, h), as
+// decode_tile deals them.
+int64_t tile_grid(const Params &p, int64_t ngroups_here) {
+  const int64_t hpg = p.H / p.G;
+  if (p.cu_seqlens) {
+    const int64_t units = p.batch * p.G * ngroups_here;
+    return 8 * hpg * ((units + 7) / 8);
+  }
+  return 8 * ((p.batch * p.H * ngroups_here + 7) / 8);
+}
+
 template <int Q, int N, bool F32, class IO>
 ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, const ssd_desc *d) {
   const int64_t bh = prm.batch * prm.H;
+  const int64_t g2 = tile_grid(prm, pl.ngroups);  // the largest grid, checked before any launch
+  if (g2 > (int64_t)UINT32_MAX) return SSD_ERR_UNSUPPORTED;
   if (pl.ngroups > 1) {
-    const int64_t t1 = bh * (pl.ngroups - 1);
-    const int64_t g1 = 8 * ((t1 + 7) / 8);
+    const int64_t g1 = tile_grid(prm, pl.ngroups - 1);
     hipLaunchKernelGGL((ssd_group_state_kernel<Q, N, F32, IO>), dim3((unsigned)g1), dim3(256),
                        0, stream, prm);
     if (prm.chained)
       hipLaunchKernelGGL((ssd_group_passing_kernel<N, main_waves<Q>()>),
                          dim3((unsigned)(bh * (kP * N / 256))), dim3(256), 0, stream, prm);
   }
-  const int64_t t2 = bh * pl.ngroups;
-  const int64_t g2 = 8 * ((t2 + 7) / 8);
   if (d->ev_main_begin && hipEventRecord(static_cast<hipEvent_t>(d->ev_main_begin), stream) != hipSuccess)
     return SSD_ERR_LAUNCH;
   // 4-wave workgroups (two per CU) for chunks of 64 and 128 tokens; 8 waves
@@ -1234,7 +1300,8 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B
   if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(out) ||
       (d->z && !aligned16(d->z)) || !aligned16(dt) ||
       (d->initial_state && !aligned16(d->initial_state)) ||
-      (return_final_state && !aligned16(final_state)))
+      (return_final_state && !aligned16(final_state)) ||
+      ((uintptr_t)d->cu_seqlens & 3u) != 0)
     return SSD_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, chunk);
   const size_t need = pl.total();
@@ -1257,8 +1324,10 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B
   char *ws = static_cast<char *>(d->workspace);
   prm.grp_state = pl.state_bytes ? reinterpret_cast<float *>(ws) : nullptr;
   prm.grp_lam = pl.lam_bytes ? reinterpret_cast<float *>(ws + pl.state_bytes) : nullptr;
+  prm.cu_seqlens = d->cu_seqlens;
   prm.batch = d->batch;
   prm.L = d->seqlen;
+  prm.Q = (int)chunk;
   prm.H = d->nheads;
   prm.G = d->ngroups;
   prm.nc = pl.nc;

@@ -44,11 +44,11 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(bnd.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), f"{name} not exported"
-    assert lib.ssd_abi_version() == 1
+    assert lib.ssd_abi_version() == 2
 
 
 def test_desc_layout_matches_c(lib):
-    assert ctypes.sizeof(bnd.SsdDesc) == 136
+    assert ctypes.sizeof(bnd.SsdDesc) == 152
     d = bnd.SsdDesc()
     ctypes.memset(ctypes.byref(d), 0x5A, ctypes.sizeof(d))
     lib.ssd_desc_init(ctypes.byref(d), 3, 5, 7, 64, 128, 7)
@@ -58,7 +58,8 @@ def test_desc_layout_matches_c(lib):
     assert d.dt_min == 0.0 and math.isinf(d.dt_max)
     assert d.z is None and d.dt_bias is None and d.initial_state is None and d.workspace is None
     assert d.workspace_bytes == 0 and d.chunks_per_wg == 0 and d.reserved == 0
-    assert d.ev_main_begin is None and d.ev_main_end is None
+    assert d.ev_main_begin is None and d.ev_main_end is None and d.cu_seqlens is None
+    assert d.packed_tokens == 0
 
 
 def test_status_strings(lib):
@@ -153,12 +154,13 @@ def test_workspace_size_errors(lib):
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload_plans(lib, name):
     w = WORKLOADS[name]
-    d = bnd.make_desc(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups)
+    # packed workloads plan for their longest sequence, one row per sequence
+    d = bnd.make_desc(w.nseq, w.max_len, w.nheads, w.headdim, w.dstate, w.ngroups)
     cpg, ng = ssd.plan(d, w.chunk)
-    nc = -(-w.seqlen // w.chunk)
+    nc = -(-w.max_len // w.chunk)
     assert 1 <= cpg <= nc and ng == -(-nc // cpg)
     ws = ssd.workspace_size(d, w.chunk)
-    slots = w.batch * w.nheads * (ng - 1)
+    slots = w.nseq * w.nheads * (ng - 1)
     if ng == 1:
         assert ws == 0                          # one group per sequence: no workspace
     else:                                       # group states and group decays
@@ -196,6 +198,26 @@ def test_rmsnorm_binding_rejects_cpu_tensors():
     x = torch.zeros(2, 8)
     with pytest.raises(ValueError):
         ssd.rmsnorm_gated(x, None, torch.ones(8), 2)
+
+
+def test_packed_plan_spreads_uneven_lengths(lib):
+    # 16 sequences, the longest 2048 tokens, 8192 in all, 16 heads, chunk 128:
+    # about 72 chunks x 16 heads over 512 workgroup slots -> 2 chunks each
+    d = _desc(B=16, L=2048, H=16, N=128, G=4)
+    d.cu_seqlens = FAKE
+    d.packed_tokens = 8192
+    assert ssd.plan(d, 128) == (2, 8)
+    d.packed_tokens = 0                          # unknown: as if all were 2048 long
+    assert ssd.plan(d, 128)[0] == 8              # (256 + 8) x 16 / 512
+    d.packed_tokens = -1
+    with pytest.raises(ValueError):
+        ssd.plan(d, 128)
+
+
+def test_misaligned_cu_seqlens(lib):
+    d = _desc()
+    d.cu_seqlens = FAKE + 2
+    assert _call(lib, d) == bnd.SSD_ERR_INVALID_ARG
 
 
 def test_product_path_does_not_touch_oracle():

@@ -14,7 +14,7 @@ D and z ~ N(0,1); the initial state is 0.1 * N(0,1).
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, Optional
+from typing import Dict, Optional, Sequence, Tuple
 
 import torch
 
@@ -34,10 +34,33 @@ class Workload:
     has_h0: bool = False
     io_dtype: str = "f32"       # dtype of x, B, C ("f32" or "bf16")
     seed: int = 20260
+    # packed variable-length sequences: their lengths (batch is then 1 and
+    # seqlen their sum, the packed token axis); empty for dense batches
+    seqlens: Tuple[int, ...] = ()
 
     @property
     def tokens(self) -> int:
         return self.batch * self.seqlen
+
+    @property
+    def packed(self) -> bool:
+        return len(self.seqlens) > 0
+
+    @property
+    def nseq(self) -> int:
+        """Rows of the call: sequences when packed, else batch rows."""
+        return len(self.seqlens) if self.packed else self.batch
+
+    @property
+    def max_len(self) -> int:
+        return max(self.seqlens) if self.packed else self.seqlen
+
+    def cu_seqlens(self) -> torch.Tensor:
+        """int32 [nseq+1] start offsets of the packed sequences (CPU)."""
+        cu = [0]
+        for n in self.seqlens:
+            cu.append(cu[-1] + n)
+        return torch.tensor(cu, dtype=torch.int32)
 
     def shape_str(self) -> str:
         return (f"[{self.batch},{self.seqlen},{self.nheads},{self.headdim},"
@@ -55,6 +78,11 @@ WORKLOADS: Dict[str, Workload] = {
     "long": Workload("long", 1, 16384, 32, 64, 128, 256, 1, has_D=True, seed=20263),
     "gated": Workload("gated", 2, 8192, 128, 64, 128, 256, 8, has_D=True, has_z=True,
                       has_h0=True, io_dtype="bf16", seed=20264),
+    # the headline's 8192 tokens and heads as 16 packed sequences with a
+    # long-tailed length mix (most lengths not a multiple of the chunk)
+    "varlen": Workload("varlen", 1, 8192, 16, 64, 128, 128, 4, has_D=True, has_h0=True,
+                       seed=20265, seqlens=(2048, 1536, 1024, 768, 640, 512, 384, 256, 200, 180,
+                                            160, 140, 130, 110, 64, 40)),
 }
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -79,15 +107,36 @@ def make_inputs(w: Workload, seed: Optional[int] = None, device: str = "cpu",
     Cm = torch.randn(Bsz, L, G, N, generator=g, dtype=f32)
     D = torch.randn(H, generator=g, dtype=f32) if w.has_D else None
     z = torch.randn(Bsz, L, H, P, generator=g, dtype=f32) if w.has_z else None
-    h0 = 0.1 * torch.randn(Bsz, H, P, N, generator=g, dtype=f32) if w.has_h0 else None
+    h0 = 0.1 * torch.randn(w.nseq, H, P, N, generator=g, dtype=f32) if w.has_h0 else None
     io = _TORCH_DTYPES[w.io_dtype]
     x, Bm, Cm = x.to(io), Bm.to(io), Cm.to(io)
     if z is not None:
         z = z.to(z_dtype)
     out = {"x": x, "dt": dt, "A": A, "B": Bm, "C": Cm, "D": D, "z": z, "initial_states": h0}
+    if w.packed:
+        out["cu_seqlens"] = w.cu_seqlens()
     if device != "cpu":
         out = {k: (None if v is None else v.to(device)) for k, v in out.items()}
     return out
+
+
+def packed_inputs(seqlens: Sequence[int], H: int, P: int, N: int, G: int, seed: int,
+                  has_D: bool = False, has_z: bool = False, has_h0: bool = False,
+                  io_dtype: str = "f32", dt_bias: bool = False) -> Dict[str, Optional[torch.Tensor]]:
+    """Packed variable-length inputs of a small shape: x [1,T,H,P], dt
+    [1,T,H], B/C [1,T,G,N], initial states [nseq,H,P,N], cu_seqlens int32
+    [nseq+1]; same distributions as the workloads."""
+    T = int(sum(seqlens))
+    w = Workload("adhoc", 1, T, H, P, N, 64, G, has_D=has_D, has_z=has_z, has_h0=has_h0,
+                 io_dtype=io_dtype, seed=seed, seqlens=tuple(int(n) for n in seqlens))
+    d = make_inputs(w)
+    if dt_bias:
+        g = torch.Generator(device="cpu")
+        g.manual_seed(seed + 7919)
+        d["dt_bias"] = -torch.rand(H, generator=g, dtype=torch.float32)
+    else:
+        d["dt_bias"] = None
+    return d
 
 
 def random_inputs(Bsz: int, L: int, H: int, P: int, N: int, G: int, seed: int,
