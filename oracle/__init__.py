@@ -15,9 +15,12 @@ Contents
   varlen     : ``ssd_varlen`` -- packed variable-length sequences (state reset
                at each cu_seqlens start), the recurrence per sequence, and
                ``ssd_quadratic_seq_idx``, the same as one masked matrix.
+  conv1d     : ``causal_conv1d`` -- the depthwise causal conv1d + bias + SiLU
+               that precedes the SSD (fp64 NumPy).
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``,
-``tests/test_oracle_rmsnorm.py`` or ``tests/test_oracle_varlen.py``
+``tests/test_oracle_rmsnorm.py``, ``tests/test_oracle_varlen.py`` or
+``tests/test_oracle_conv1d.py``
 (hand-derived golden values, closed forms, cross-form equality and
 invariants); none is "parity unpinned".
 """
@@ -26,3 +29,4 @@ from .forms import (ssd_quadratic, ssd_chunked, ssd_linear_attention_closed_form
                     discretize)
 from .rmsnorm import rmsnorm_gated  # noqa: F401
 from .varlen import ssd_quadratic_seq_idx, ssd_varlen  # noqa: F401
+from .conv1d import causal_conv1d  # noqa: F401
