@@ -15,6 +15,9 @@ Prints ONE JSON line: whole-step throughput (tokens/s), plus
 ``--op rmsnorm_gated`` instead times the gated grouped RMSNorm that follows
 the SSD forward (page "ops-transformer MambaV2 算子套件", section 4.6) on the
 configuration's output shape [B*L, H*P] with G groups: a step is one launch.
+``--op causal_conv1d`` times the depthwise causal conv1d + bias + SiLU before
+it (that page, §1.4 and §4.1) on [B, H*P + 2*G*N, L], or with ``--config
+page`` on the page's own test shape [1, 10240, 1024]: a step is one launch.
 """
 from __future__ import annotations
 
@@ -28,11 +31,13 @@ import time
 
 import torch
 
-from workloads import NORM_EPS, WORKLOADS, Workload, make_inputs, norm_inputs, norm_shape
+from workloads import (CONV_WIDTH, NORM_EPS, WORKLOADS, Workload, conv_inputs, conv_shape,
+                       make_inputs, norm_inputs, norm_shape)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "SSD fwd ms & tokens/s at [B,L,H,P,N,chunk,G]; % of MFMA/HBM roofline"
 NORM_METRIC = "gated RMSNorm ms & tokens/s at [B*L, H*P], G groups; % of HBM roofline"
+CONV_METRIC = "causal conv1d ms & tokens/s at [B, D, S], width 4; % of HBM roofline"
 # Published figure for [4,2048,16,64,128,128,4]: 0.632 ms on Ascend 910B3
 # (page "Mamba-2 SSD for Ascend NPU", Benchmark table) = 4*2048/0.632e-3 tokens/s.
 PAGE_TOKENS_PER_S = {"same_device": 4 * 2048 / 0.632e-3,
@@ -307,13 +312,116 @@ def packed_cpu_baseline(w: Workload, d, budget_s: float, threads: int):
                       f"repetition(s), {t:.1f} s of fp64 recurrence on {threads} OpenMP threads"}
 
 
+def conv_bytes(B: int, D: int, S: int, W: int) -> int:
+    """x read and out written once, the taps and bias, the conv state read and
+    the final state written."""
+    return 8 * B * D * S + 4 * D * (W + 1) + 8 * B * D * (W - 1)
+
+
+def conv_cpu_baseline(B: int, D: int, S: int, seed: int, budget_s: float):
+    """The fp64 conv oracle on a bounded sample of channels, scaled to tokens/s
+    (a token is one step of all B*D channels)."""
+    from oracle import causal_conv1d as oracle_conv
+    n = min(D, 64)
+    d = conv_inputs(1, n, S, CONV_WIDTH, seed, has_state=True)
+    x, wt, b, st = (d[k].numpy() for k in ("x", "w", "bias", "conv_state"))
+    reps, t = 0, 0.0
+    while t < budget_s:
+        t0 = time.perf_counter()
+        oracle_conv(x, wt, b, st)
+        t += time.perf_counter() - t0
+        reps += 1
+    chan_steps_per_s = n * S * reps / t
+    return {"value": chan_steps_per_s / D, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} of {B * D} channel rows of {S} steps, {reps} repetition(s), {t:.1f} s "
+                      f"of fp64 numpy on one thread; scaled to B*S tokens of all D channels"}
+
+
+def conv_main(args) -> int:
+    import mamba_ssd_chunked_04_amd as ssd
+    name = args.config
+    B, D, S = conv_shape(name)
+    W = CONV_WIDTH
+    dev = "cuda:0"
+    abytes = conv_bytes(B, D, S, W)
+    n_sets = args.sets or max(1, min(16, math.ceil(2 * 512e6 / abytes)))
+    print(f"[bench] causal conv1d {name}: B={B} D={D} S={S} W={W} sets={n_sets}",
+          file=sys.stderr, flush=True)
+    seed0 = (WORKLOADS[name].seed if name in WORKLOADS else 20269) * 1000 + 700
+    sets = []
+    for k in range(n_sets):
+        d = conv_inputs(B, D, S, W, seed0 + k, device=dev, has_state=True)
+        d["out"] = torch.empty_like(d["x"])
+        d["fin"] = torch.empty_like(d["conv_state"])
+        sets.append(d)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+    copy_calibration(args.copy_calibration_mb, dev)
+
+    def step(k):
+        d = sets[k % n_sets]
+        ssd.causal_conv1d(d["x"], d["w"], d["bias"], d["conv_state"], out=d["out"],
+                          return_final_state=True, final_state=d["fin"])
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    # one launch per step: the kernel's mean duration over the back-to-back
+    # timed launches, between two events on the launch stream
+    K = args.steps
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.record(e0, stream)
+    for k in range(K):
+        step(k)
+    ev.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kmean = ev.elapsed_ms(e0, e1) / K
+    ev.destroy(e0)
+    ev.destroy(e1)
+    achieved = abytes / (kmean * 1e-3) / 1e9
+    rec = {
+        "metric": CONV_METRIC,
+        "value": B * S / (wall / K),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"causal conv1d {name} [B={B}, D={D}, S={S}]", "B": B, "D": D,
+                   "S": S, "W": W, "bias": True, "conv_state": True, "activation": "silu",
+                   "input_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(name, "causal_conv1d_vec_kernel",
+                                                 "traffic_conv1d.json"),
+                     "kernel": "causal_conv1d_vec_kernel", "kernel_ms": kmean,
+                     "algorithmic_bytes": abytes},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = conv_cpu_baseline(B, D, S, seed0, args.cpu_baseline_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="same_device", choices=sorted(WORKLOADS))
-    ap.add_argument("--op", default="ssd_fwd", choices=["ssd_fwd", "rmsnorm_gated"])
+    ap.add_argument("--config", default="same_device", choices=sorted(WORKLOADS) + ["page"],
+                    help="workload; 'page' is the conv1d test shape of --op causal_conv1d")
+    ap.add_argument("--op", default="ssd_fwd", choices=["ssd_fwd", "rmsnorm_gated",
+                                                        "causal_conv1d"])
     ap.add_argument("--mma", default="f16", choices=["f16", "f32"])
     ap.add_argument("--chunks-per-wg", type=int, default=0)
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = auto)")
@@ -334,9 +442,14 @@ def main(argv=None):
 
     import mamba_ssd_chunked_04_amd as ssd
     ssd.load_library()
+    torch.cuda.set_device(0)
+    if args.op == "causal_conv1d":
+        return conv_main(args)
+    if args.config not in WORKLOADS:
+        print(f"--config {args.config} is a conv1d shape only", file=sys.stderr)
+        return 2
     w = WORKLOADS[args.config]
     dev = "cuda:0"
-    torch.cuda.set_device(0)
     if args.op == "rmsnorm_gated":
         return norm_main(args, w)
     print(f"[bench] workload {w.name} {w.shape_str()} mma={args.mma}", file=sys.stderr, flush=True)

@@ -176,6 +176,30 @@ ssd_status ssd_rmsnorm_gated(const float *x, const float *z, const float *w,
                              int64_t rows, int64_t dim, int64_t ngroups,
                              float eps, float *out, void *stream);
 
+/* Depthwise causal conv1d with bias and SiLU, the step before the SSD (page
+ * "ops-transformer MambaV2 算子套件", §1.4 and §4.1, mamba2_causal_conv1d):
+ *
+ *   out[b,d,t] = act(bias[d] + sum_{k<W} w[d,k] * xx[b,d,t-(W-1)+k])
+ *
+ * with act = SiLU (activation 1) or none (0), and xx = x preceded by the
+ * W-1 steps of the conv state x_prev (zeros when x_prev is NULL): tap W-1
+ * weighs the current step, as in a conv1d padded by W-1 and cut to S steps.
+ *   x, out      [B, D, S] fp32     w [D, W] fp32     bias [D] fp32 or NULL
+ *   x_prev      [B, D, W-1] fp32 or NULL (the steps before t = 0)
+ *   final_state [B, D, W-1] fp32 or NULL: receives the last W-1 steps of
+ *               xx (the state for the next call); it may be x_prev itself
+ *               (an in-place state update) when S <= 1024.
+ * Any S >= 1; S % 4 == 0 with 16-byte aligned x and out takes the vector
+ * path.  out must not overlap x.  Errors: SSD_ERR_INVALID_ARG for a NULL
+ * x/w/out, a dim < 1, activation not 0/1, a pointer not 4-byte aligned or a
+ * forbidden overlap; SSD_ERR_UNSUPPORTED for W outside 2..4, S*4 reaching
+ * 2^31 bytes, B*D*S reaching 2^40 or ceil(B*D/4)*ceil(S/1024) reaching
+ * 2^31 workgroups. */
+ssd_status ssd_causal_conv1d(const float *x, const float *w, const float *bias,
+                             const float *x_prev, int64_t batch, int64_t dim,
+                             int64_t seqlen, int64_t width, int activation,
+                             float *out, float *final_state, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *ssd_status_str(int status);
 

@@ -19,7 +19,7 @@ SSD_MMA_F16, SSD_MMA_F32 = 0, 2
 
 # Every symbol include/ssd_mi355x.h declares.
 EXPORTED_SYMBOLS = ("ssd_desc_init", "ssd_fwd_workspace_size", "ssd_fwd_plan", "ssd_fwd",
-                    "ssd_rmsnorm_gated", "ssd_status_str", "ssd_abi_version")
+                    "ssd_rmsnorm_gated", "ssd_causal_conv1d", "ssd_status_str", "ssd_abi_version")
 
 
 class SsdDesc(ctypes.Structure):
@@ -69,6 +69,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ssd_fwd.restype = c_int
     lib.ssd_rmsnorm_gated.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_float, vp, vp]
     lib.ssd_rmsnorm_gated.restype = c_int
+    lib.ssd_causal_conv1d.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, c_int, vp, vp, vp]
+    lib.ssd_causal_conv1d.restype = c_int
     lib.ssd_status_str.argtypes = [c_int]
     lib.ssd_status_str.restype = ctypes.c_char_p
     lib.ssd_abi_version.argtypes = []
@@ -274,3 +276,44 @@ def rmsnorm_gated(x, z, weight, ngroups: int, eps: float = 1e-5, out=None):
                                                     int(ngroups), float(eps), _ptr(out),
                                                     ctypes.c_void_p(st)), "ssd_rmsnorm_gated")
     return out
+
+
+def causal_conv1d(x, weight, bias=None, conv_state=None, activation: str = "silu", out=None,
+                  return_final_state: bool = False, final_state=None):
+    """Depthwise causal conv1d (+ bias, + SiLU) over the last axis, on the
+    current torch stream.
+
+    x: [B, D, S] float32 GPU tensor; weight: [D, W] (W in 2..4); bias: [D]
+    or None; conv_state: [B, D, W-1] steps before t = 0, or None (zeros).
+    Returns ``out``, or ``(out, final_state)`` with ``return_final_state``
+    (``final_state`` may be ``conv_state`` itself when S <= 1024).
+    """
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dim() != 3:
+        raise ValueError("x must be a [B, D, S] GPU tensor")
+    Bsz, D, S = x.shape
+    if weight.dim() != 2 or weight.shape[0] != D:
+        raise ValueError("weight must be [D, W]")
+    W = weight.shape[1]
+    act = {"silu": 1, None: 0, "none": 0}[activation]
+    if out is None:
+        out = torch.empty_like(x)
+    if return_final_state and final_state is None:
+        final_state = torch.empty(Bsz, D, W - 1, device=x.device, dtype=torch.float32)
+    shapes = ((bias, (D,)), (conv_state, (Bsz, D, W - 1)), (out, (Bsz, D, S)),
+              (final_state if return_final_state else None, (Bsz, D, W - 1)))
+    for t, shp in shapes:
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"expected shape {shp}, got {tuple(t.shape)}")
+    for t in (x, weight, bias, conv_state, out, final_state):
+        if t is None:
+            continue
+        if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous float32 on the GPU of x")
+    with torch.cuda.device(x.device):
+        st = torch.cuda.current_stream(x.device).cuda_stream
+        _raise_for(load_library().ssd_causal_conv1d(
+            _ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state), Bsz, D, S, W, act, _ptr(out),
+            _ptr(final_state) if return_final_state else None, ctypes.c_void_p(st)),
+            "ssd_causal_conv1d")
+    return (out, final_state) if return_final_state else out

@@ -193,6 +193,26 @@ def test_rmsnorm_unsupported(lib, kw):
     assert _rms(lib, **kw) == bnd.SSD_ERR_UNSUPPORTED
 
 
+def _conv(lib, x=FAKE, w=FAKE, bias=None, xp=None, B=2, D=8, S=64, W=4, act=1, out=FAKE * 2,
+          fin=None):
+    return lib.ssd_causal_conv1d(x, w, bias, xp, B, D, S, W, act, out, fin, None)
+
+
+@pytest.mark.parametrize("kw", [dict(x=None), dict(w=None), dict(out=None), dict(B=0), dict(D=0),
+                                dict(S=0), dict(W=0), dict(act=2), dict(x=FAKE + 2),
+                                dict(bias=FAKE + 1), dict(out=FAKE),        # out == x
+                                dict(xp=FAKE * 3, fin=FAKE * 3, S=2048)],  # in place, 2 blocks
+                         ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_conv1d_invalid_args(lib, kw):
+    assert _conv(lib, **kw) == bnd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(W=1), dict(W=5), dict(S=1 << 29)],
+                         ids=["W1", "W5", "S2^29"])
+def test_conv1d_unsupported(lib, kw):
+    assert _conv(lib, **kw) == bnd.SSD_ERR_UNSUPPORTED
+
+
 def test_rmsnorm_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros(2, 8)

@@ -187,3 +187,37 @@ def norm_inputs(rows: int, dim: int, seed: int, has_z: bool = True,
     z = torch.randn(rows, dim, generator=g, device=device, dtype=f32) if has_z else None
     wt = 1.0 + 0.1 * torch.randn(dim, generator=g, device=device, dtype=f32)
     return {"x": x, "z": z, "w": wt}
+
+
+# ------------------------------------------------------------------ causal conv1d
+# The depthwise causal conv1d before the SSD (page "ops-transformer MambaV2
+# 算子套件", §1.4 and §4.1) runs on x [B, D, S] with D channels.  Its test
+# shape on that page is B=1, D=10240, S=1024, W=4 ("page"); before an SSD
+# workload w it runs over the channels that feed x, B and C,
+# D = H*P + 2*G*N, with S = L.  x ~ N(0,1); weight and bias ~ U(-1/sqrt(W),
+# 1/sqrt(W)) (the default initialisation of a grouped conv1d with W taps per
+# channel; the page gives no distribution); conv state ~ N(0,1).
+CONV_WIDTH = 4
+
+
+def conv_shape(name: str):
+    """(B, D, S) of the conv workload ``name``: "page" or an SSD workload."""
+    if name == "page":
+        return 1, 10240, 1024
+    w = WORKLOADS[name]
+    return w.batch, w.nheads * w.headdim + 2 * w.ngroups * w.dstate, w.seqlen
+
+
+def conv_inputs(Bsz: int, D: int, S: int, W: int, seed: int, device: str = "cpu",
+                has_bias: bool = True, has_state: bool = False) -> Dict[str, Optional[torch.Tensor]]:
+    """x [B,D,S], weight [D,W], bias [D] (or None), conv_state [B,D,W-1] (or
+    None), fp32, drawn in that order from a generator on ``device``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    f32 = torch.float32
+    bound = 1.0 / W ** 0.5
+    x = torch.randn(Bsz, D, S, generator=g, device=device, dtype=f32)
+    wt = (torch.rand(D, W, generator=g, device=device, dtype=f32) * 2 - 1) * bound
+    b = (torch.rand(D, generator=g, device=device, dtype=f32) * 2 - 1) * bound if has_bias else None
+    st = torch.randn(Bsz, D, W - 1, generator=g, device=device, dtype=f32) if has_state else None
+    return {"x": x, "w": wt, "bias": b, "conv_state": st}
