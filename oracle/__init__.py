@@ -17,10 +17,12 @@ Contents
                ``ssd_quadratic_seq_idx``, the same as one masked matrix.
   conv1d     : ``causal_conv1d`` -- the depthwise causal conv1d + bias + SiLU
                that precedes the SSD (fp64 NumPy).
+  backward   : ``ssd_grads`` -- the gradients of the SSD forward, by
+               autograd over the token recurrence in PyTorch fp64.
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``,
-``tests/test_oracle_rmsnorm.py``, ``tests/test_oracle_varlen.py`` or
-``tests/test_oracle_conv1d.py``
+``tests/test_oracle_rmsnorm.py``, ``tests/test_oracle_varlen.py``,
+``tests/test_oracle_conv1d.py`` or ``tests/test_oracle_backward.py``
 (hand-derived golden values, closed forms, cross-form equality and
 invariants); none is "parity unpinned".
 """
@@ -30,3 +32,4 @@ from .forms import (ssd_quadratic, ssd_chunked, ssd_linear_attention_closed_form
 from .rmsnorm import rmsnorm_gated  # noqa: F401
 from .varlen import ssd_quadratic_seq_idx, ssd_varlen  # noqa: F401
 from .conv1d import causal_conv1d  # noqa: F401
+from .backward import ssd_grads  # noqa: F401
