@@ -15,6 +15,8 @@ Prints ONE JSON line: whole-step throughput (tokens/s), plus
 ``--op rmsnorm_gated`` instead times the gated grouped RMSNorm that follows
 the SSD forward (page "ops-transformer MambaV2 算子套件", section 4.6) on the
 configuration's output shape [B*L, H*P] with G groups: a step is one launch.
+``--op ssd_bwd`` times the SSD backward (fp32; P = N = chunk = 64, so the
+training-shape workload h256 by default): a step is the whole backward.
 ``--op causal_conv1d`` times the depthwise causal conv1d + bias + SiLU before
 it (that page, §1.4 and §4.1) on [B, H*P + 2*G*N, L], or with ``--config
 page`` on the page's own test shape [1, 10240, 1024]: a step is one launch.
@@ -38,6 +40,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "SSD fwd ms & tokens/s at [B,L,H,P,N,chunk,G]; % of MFMA/HBM roofline"
 NORM_METRIC = "gated RMSNorm ms & tokens/s at [B*L, H*P], G groups; % of HBM roofline"
 CONV_METRIC = "causal conv1d ms & tokens/s at [B, D, S], width 4; % of HBM roofline"
+BWD_METRIC = "SSD bwd ms & tokens/s at [B,L,H,P,N,chunk,G] (fp32, P=N=chunk=64); % of fp32 roofline"
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published
 # Published figure for [4,2048,16,64,128,128,4]: 0.632 ms on Ascend 910B3
 # (page "Mamba-2 SSD for Ascend NPU", Benchmark table) = 4*2048/0.632e-3 tokens/s.
 PAGE_TOKENS_PER_S = {"same_device": 4 * 2048 / 0.632e-3,
@@ -413,6 +417,108 @@ def conv_main(args) -> int:
     return 0
 
 
+def bwd_flops_per_chunk() -> int:
+    """fp32 flops of the backward main kernel per (b, h, 64-token chunk): nine
+    64x64x64 products (C B^T, dy x^T, W1^T dy, B G^T, W2^T C, x G, W2 B, dy S,
+    dy^T diag C)."""
+    return 9 * 2 * 64 ** 3
+
+
+def bwd_main(args) -> int:
+    import mamba_ssd_chunked_04_amd as ssd
+    name = args.config if args.config != "same_device" else "h256"
+    w = WORKLOADS[name]
+    if (w.headdim, w.dstate, w.chunk) != (64, 64, 64) or w.packed or w.has_z:
+        print(f"--op ssd_bwd needs P = N = chunk = 64 without z: {name} is not", file=sys.stderr)
+        return 2
+    dev = "cuda:0"
+    print(f"[bench] SSD backward {w.name} {w.shape_str()}", file=sys.stderr, flush=True)
+    d = {k: (None if v is None else v.to(dev)) for k, v in make_inputs(w).items()}
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed * 1000 + 900)
+    dout = torch.randn(w.batch, w.seqlen, w.nheads, 64, generator=g, device=dev)
+    dfin = torch.randn(w.batch, w.nheads, 64, 64, generator=g, device=dev)
+    call = ssd.prepare_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], dout, 64, D=d["D"],
+                           initial_states=d["initial_states"], dfinal_state=dfin,
+                           dt_softplus=True)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+    for _ in range(args.warmup):
+        call.launch(stream)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(ev.create(), ev.create()) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        call.desc.ev_main_begin, call.desc.ev_main_end = evs[k][0].value, evs[k][1].value
+        call.launch(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call.desc.ev_main_begin = call.desc.ev_main_end = None
+    main_ms = [ev.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+    kmean = sum(main_ms) / len(main_ms)
+    nc = -(-w.seqlen // 64)
+    flops = bwd_flops_per_chunk() * w.batch * w.nheads * nc
+    achieved = flops / (kmean * 1e-3) / 1e12
+    rec = {
+        "metric": BWD_METRIC,
+        "value": w.tokens / (wall / K),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"SSD backward {w.name} {w.shape_str()}", "B": w.batch,
+                   "L": w.seqlen, "H": w.nheads, "P": 64, "N": 64, "chunk": 64, "G": w.ngroups,
+                   "D": w.has_D, "initial_state": w.has_h0, "dfinal_state": True},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "ssd_bwd_chunk_kernel", "kernel_ms": kmean,
+                     "algorithmic_flops": flops},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = bwd_cpu_baseline(w, args.cpu_baseline_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def bwd_cpu_baseline(w: Workload, budget_s: float):
+    """The fp64 autograd backward oracle on one sequence of one group's heads
+    (one batch row, H/G heads) of the workload, repeated to about budget_s,
+    scaled to tokens/s of the whole workload."""
+    from oracle import ssd_grads
+    from workloads import random_inputs
+    hpg = w.nheads // w.ngroups
+    L = min(w.seqlen, 512)
+    d = random_inputs(1, L, hpg, 64, 64, 1, seed=w.seed, has_D=w.has_D, has_h0=w.has_h0)
+    g = torch.Generator().manual_seed(5)
+    dout = torch.randn(1, L, hpg, 64, generator=g)
+    reps, t = 0, 0.0
+    while t < budget_s:
+        t0 = time.perf_counter()
+        ssd_grads(d["x"], d["dt"], d["A"], d["B"], d["C"], dout, D=d["D"],
+                  initial_states=d["initial_states"], dt_softplus=True)
+        t += time.perf_counter() - t0
+        reps += 1
+    heads_tokens_per_s = hpg * L * reps / t
+    return {"value": heads_tokens_per_s / w.nheads, "unit": "tokens/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{L} tokens of one sequence of the {hpg} heads of one group (same "
+                      f"distributions), "
+                      f"{reps} repetition(s), {t:.1f} s of fp64 autograd; scaled to tokens/s "
+                      f"of all {w.nheads} heads"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -420,7 +526,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="same_device", choices=sorted(WORKLOADS) + ["page"],
                     help="workload; 'page' is the conv1d test shape of --op causal_conv1d")
-    ap.add_argument("--op", default="ssd_fwd", choices=["ssd_fwd", "rmsnorm_gated",
+    ap.add_argument("--op", default="ssd_fwd", choices=["ssd_fwd", "ssd_bwd", "rmsnorm_gated",
                                                         "causal_conv1d"])
     ap.add_argument("--mma", default="f16", choices=["f16", "f32"])
     ap.add_argument("--chunks-per-wg", type=int, default=0)
@@ -445,6 +551,8 @@ def main(argv=None):
     torch.cuda.set_device(0)
     if args.op == "causal_conv1d":
         return conv_main(args)
+    if args.op == "ssd_bwd":
+        return bwd_main(args)
     if args.config not in WORKLOADS:
         print(f"--config {args.config} is a conv1d shape only", file=sys.stderr)
         return 2

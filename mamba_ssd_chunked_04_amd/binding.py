@@ -19,7 +19,8 @@ SSD_MMA_F16, SSD_MMA_F32 = 0, 2
 
 # Every symbol include/ssd_mi355x.h declares.
 EXPORTED_SYMBOLS = ("ssd_desc_init", "ssd_fwd_workspace_size", "ssd_fwd_plan", "ssd_fwd",
-                    "ssd_rmsnorm_gated", "ssd_causal_conv1d", "ssd_status_str", "ssd_abi_version")
+                    "ssd_bwd_workspace_size", "ssd_bwd", "ssd_rmsnorm_gated", "ssd_causal_conv1d",
+                    "ssd_status_str", "ssd_abi_version")
 
 
 class SsdDesc(ctypes.Structure):
@@ -69,6 +70,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ssd_fwd.restype = c_int
     lib.ssd_rmsnorm_gated.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_float, vp, vp]
     lib.ssd_rmsnorm_gated.restype = c_int
+    lib.ssd_bwd_workspace_size.argtypes = [dp, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssd_bwd_workspace_size.restype = c_int
+    lib.ssd_bwd.argtypes = [vp] * 6 + [i64, c_int] + [vp] * 10 + [vp, dp]
+    lib.ssd_bwd.restype = c_int
     lib.ssd_causal_conv1d.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, c_int, vp, vp, vp]
     lib.ssd_causal_conv1d.restype = c_int
     lib.ssd_status_str.argtypes = [c_int]
@@ -317,3 +322,79 @@ def causal_conv1d(x, weight, bias=None, conv_state=None, activation: str = "silu
             _ptr(final_state) if return_final_state else None, ctypes.c_void_p(st)),
             "ssd_causal_conv1d")
     return (out, final_state) if return_final_state else out
+
+
+class SsdBwdCall:
+    """One prepared ``ssd_bwd`` call over fixed tensors (for repeated launches)."""
+
+    def __init__(self, args, desc: SsdDesc, keep, grads):
+        self._args = args
+        self.desc = desc
+        self._keep = keep
+        self.grads = grads
+
+    def launch(self, stream: int) -> None:
+        a = self._args
+        st = load_library().ssd_bwd(*a, ctypes.c_void_p(stream), ctypes.byref(self.desc))
+        _raise_for(st, "ssd_bwd")
+
+
+def prepare_bwd(x, dt, A, B, C, dout, chunk_size: int = 64, D=None, dt_bias=None,
+                initial_states=None, dfinal_state=None, dt_softplus: bool = False,
+                dt_limit: Tuple[float, float] = (0.0, math.inf)):
+    """Validate, allocate the gradients and the workspace, build an SsdBwdCall.
+
+    fp32 tensors in the ssd_fwd layouts (no z gate).  ``call.grads`` holds dx,
+    ddt, dA, dB, dC and, for the optional inputs given, dD, ddt_bias,
+    dinitial_states.
+    """
+    import torch
+    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    dev = x.device
+    Bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    shapes = (("dt", dt, (Bsz, L, H)), ("A", A, (H,)), ("B", B, (Bsz, L, G, N)),
+              ("C", C, (Bsz, L, G, N)), ("dout", dout, (Bsz, L, H, P)), ("D", D, (H,)),
+              ("dt_bias", dt_bias, (H,)), ("initial_states", initial_states, (Bsz, H, P, N)),
+              ("dfinal_state", dfinal_state, (Bsz, H, P, N)))
+    for name, t, shp in shapes:
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} must have shape {shp}")
+    for t in (x, dt, A, B, C, dout, D, dt_bias, initial_states, dfinal_state):
+        if t is not None and (t.dtype != torch.float32 or t.device != dev or not t.is_contiguous()):
+            raise ValueError("all tensors must be contiguous float32 on the same GPU")
+    desc = make_desc(Bsz, L, H, P, N, G)
+    desc.mma = SSD_MMA_F32
+    desc.dt_min, desc.dt_max = float(dt_limit[0]), float(dt_limit[1])
+    desc.dt_bias, desc.initial_state = _ptr(dt_bias), _ptr(initial_states)
+    n = ctypes.c_size_t(0)
+    _raise_for(load_library().ssd_bwd_workspace_size(ctypes.byref(desc), int(chunk_size),
+                                                     ctypes.byref(n)), "ssd_bwd_workspace_size")
+    ws = torch.empty(int(n.value), device=dev, dtype=torch.uint8)
+    desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
+    e = lambda *s: torch.empty(*s, device=dev, dtype=torch.float32)
+    grads = {"dx": e(Bsz, L, H, P), "ddt": e(Bsz, L, H), "dA": e(H), "dB": e(Bsz, L, G, N),
+             "dC": e(Bsz, L, G, N), "dD": e(H) if D is not None else None,
+             "ddt_bias": e(H) if dt_bias is not None else None,
+             "dinitial_states": e(Bsz, H, P, N) if initial_states is not None else None}
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk_size),
+            int(bool(dt_softplus)), _ptr(dout), _ptr(dfinal_state),
+            *(_ptr(grads[k]) for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "ddt_bias",
+                                       "dinitial_states")))
+    keep = (x, dt, A, B, C, dout, D, dt_bias, initial_states, dfinal_state, ws)
+    return SsdBwdCall(args, desc, keep, grads)
+
+
+def ssd_bwd(x, dt, A, B, C, dout, chunk_size: int = 64, D=None, dt_bias=None,
+            initial_states=None, dfinal_state=None, dt_softplus: bool = False,
+            dt_limit: Tuple[float, float] = (0.0, math.inf)):
+    """SSD backward on the current torch stream; returns the dict of gradients."""
+    import torch
+    call = prepare_bwd(x, dt, A, B, C, dout, chunk_size, D=D, dt_bias=dt_bias,
+                       initial_states=initial_states, dfinal_state=dfinal_state,
+                       dt_softplus=dt_softplus, dt_limit=dt_limit)
+    with torch.cuda.device(x.device):
+        call.launch(torch.cuda.current_stream(x.device).cuda_stream)
+    return call.grads

@@ -1,7 +1,8 @@
 """Compile the HIP library for gfx950, in-tree.
 
 Produces mamba_ssd_chunked_04_amd/libssd_mi355x.so from the HIP sources in
-csrc/ (the SSD forward, the gated RMSNorm and the causal conv1d) with hipcc.  Packed-fp32 instruction selection is switched off for all device
+csrc/ (the SSD forward and backward, the gated RMSNorm and the causal
+conv1d) with hipcc.  Packed-fp32 instruction selection is switched off for all device
 code (-Xclang -target-feature -Xclang -packed-fp32-ops).
 """
 from __future__ import annotations
@@ -14,7 +15,7 @@ import time
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
 SRCS = tuple(os.path.join(PKG_DIR, "csrc", f)
-             for f in ("ssd_fwd.hip", "rmsnorm_gated.hip", "causal_conv1d.hip"))
+             for f in ("ssd_fwd.hip", "ssd_bwd.hip", "rmsnorm_gated.hip", "causal_conv1d.hip"))
 HEADER = os.path.join(REPO_DIR, "include", "ssd_mi355x.h")
 LIB = os.path.join(PKG_DIR, "libssd_mi355x.so")
 ARCH = "gfx950"

@@ -1,0 +1,576 @@
+// Backward pass of the SSD chunked forward for MI355X (gfx950), fp32.
+//
+// Gradients of L = <dout, out> + <dfinal_state, final_state> for the forward
+// of page "ops-transformer MambaV2 算子套件" §1.1/§1.3 (token recurrence and
+// its chunked form) with the tensor semantics of page "Mamba-2 SSD for Ascend
+// NPU", "Implementation"; that page's "AscendC training" section and
+// "Limitations and roadmap" scope a first backward to contiguous
+// P = N = chunk = 64 in FP32, which is the scope here (no z gate).
+//
+// Per chunk, with delta_j the discretised step, Lam the in-chunk inclusive
+// prefix of delta*A (natural log units), S the state entering the chunk and
+// G the gradient of the state leaving it:
+//   y_i   = sum_{j<=i} (C_i.B_j) e^{Lam_i-Lam_j} delta_j x_j + e^{Lam_i} C_i S + D x_i
+//   S_out = e^{Lam_end} S + sum_j e^{Lam_end-Lam_j} delta_j x_j (outer) B_j
+// so, with W1_ij = (C_i.B_j) e^{Lam_i-Lam_j} delta_j and
+// W2_ij = (dy_i.x_j) e^{Lam_i-Lam_j} delta_j (j <= i):
+//   dx_j = sum_i W1_ij dy_i + delta_j e^{Lam_end-Lam_j} G B_j + D dy_j
+//   dB_j = sum_i W2_ij C_i + delta_j e^{Lam_end-Lam_j} G^T x_j
+//   dC_i = sum_j W2_ij B_j + e^{Lam_i} S^T dy_i
+//   G_in = e^{Lam_end} G + sum_i e^{Lam_i} dy_i (outer) C_i       (gradient of S)
+// and the step and decay gradients through Lam (reverse in-chunk cumsum of
+// dLam gives d(delta*A)), then dt through the clamp and softplus.
+//
+// Kernels: (1) ssd_bwd_states_kernel, one workgroup per (b, h), walks the
+// chunks forward and stores the state entering each; (2) ssd_bwd_chunk_kernel,
+// one workgroup per (b, h), walks the chunks backward carrying G in LDS, all
+// products as 4x4-per-thread fp32 tiles over LDS; (3) ssd_bwd_reduce_kernel
+// sums the per-head dB/dC over the heads of a group and dA, dD, ddt_bias over
+// the batch.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/ssd_mi355x.h"
+
+namespace {
+
+constexpr int kQ = 64, kP = 64, kN = 64;  // chunk, head dim, state dim
+constexpr int kLd = 65;                   // LDS row stride of the 64x64 tiles
+constexpr uint32_t kOOB = 0x80000000u;    // a byte offset past every range
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ float ld(rsrc_t r, uint32_t byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ void st(rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, 0);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then row
+// totals broadcast to the later rows).
+__device__ __forceinline__ float wave_scan(float v) {
+  int x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true));
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true));
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true));
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true));
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
+  return v;
+}
+
+__device__ __forceinline__ float lane63(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+struct BwdParams {
+  const float *x, *dt, *A, *B, *C, *D, *dt_bias, *h0, *dout, *dfin;
+  float *dx, *ddt, *dA, *dB, *dC, *dD, *ddt_bias, *dh0;
+  float *states;        // [B*H][nc][P][N]: state entering each chunk
+  float *dBh, *dCh;     // [B][L][H][N]: per-head dB, dC
+  float *part;          // [B*H][4]: per-(b,h) dA, dD, ddt_bias partial sums
+  int64_t batch, L, H, G, nc;
+  float dt_min, dt_max;
+  int dt_softplus;
+};
+
+// Per-chunk scalars in LDS.
+struct ChunkScalars {
+  float lam[kQ], del[kQ], el[kQ], er[kQ], gfac[kQ];  // Lam, delta, e^Lam, e^{Lam_end-Lam}, ddt/ddelta
+  float lend, elend;
+};
+
+// Discretise the chunk's steps and scan Lam; wave 0 computes, everyone reads
+// after the caller's barrier.  Tokens past the sequence end get delta = 0.
+__device__ __forceinline__ void chunk_scalars(const BwdParams &p, rsrc_t rdt, uint32_t t0,
+                                              uint32_t len, uint32_t H, uint32_t h, float a_h,
+                                              float bias, ChunkScalars &cs) {
+  if (threadIdx.x >= 64) return;
+  const int j = threadIdx.x;
+  const bool valid = t0 + j < len;
+  const float u = ld(rdt, valid ? ((t0 + j) * H + h) * 4u : kOOB) + bias;
+  float sp = u, dsp = 1.f;
+  if (p.dt_softplus) {
+    const float e = __expf(-fabsf(u));
+    sp = fmaxf(u, 0.f) + log1pf(e);                       // softplus, no overflow
+    dsp = u >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);     // sigmoid(u)
+  }
+  const bool inside = sp >= p.dt_min && sp <= p.dt_max;
+  const float delta = valid ? fminf(fmaxf(sp, p.dt_min), p.dt_max) : 0.f;
+  const float lam = wave_scan(delta * a_h);
+  const float lend = lane63(lam);
+  cs.lam[j] = lam;
+  cs.del[j] = delta;
+  cs.el[j] = __expf(lam);
+  cs.er[j] = __expf(lend - lam);
+  cs.gfac[j] = (valid && inside) ? dsp : 0.f;
+  if (j == 0) {
+    cs.lend = lend;
+    cs.elend = __expf(lend);
+  }
+}
+
+// acc[r][c] += sum_k A(row0 + r, k) * B(k, col0 + c), k < 64, both in LDS:
+// A(i, k) = a[i * ars + k * aks], B(k, c) = b[k * bks + c * bcs].
+__device__ __forceinline__ void mm(const float *a, int ars, int aks, const float *b, int bks,
+                                   int bcs, int row0, int col0, float (&acc)[4][4]) {
+#pragma unroll 4
+  for (int k = 0; k < 64; ++k) {
+    float av[4], bv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) av[r] = a[(row0 + r) * ars + k * aks];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bv[c] = b[k * bks + (col0 + c) * bcs];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+  }
+}
+
+__device__ __forceinline__ void zero(float (&acc)[4][4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+}
+
+// Row-major [token][64] tile of one (b, h) chunk from a [B, L, X, 64] tensor
+// (X = H or G, column offset `slot`) into LDS, zeros past the sequence end.
+__device__ __forceinline__ void load_tile(rsrc_t r, uint32_t t0, uint32_t len, uint32_t X,
+                                          uint32_t slot, float *dst) {
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int j = e >> 6, c = e & 63;
+    dst[j * kLd + c] = ld(r, t0 + j < len ? (((t0 + j) * X + slot) * 64 + c) * 4u : kOOB);
+  }
+}
+
+// Forward pass that stores the state entering every chunk.
+__global__ __launch_bounds__(256) void ssd_bwd_states_kernel(BwdParams p) {
+  __shared__ float sX[kQ * kLd], sB[kQ * kLd];
+  __shared__ ChunkScalars cs;
+  const int64_t bh = blockIdx.x, b = bh / p.H, h = bh % p.H;
+  const int64_t g = h / (p.H / p.G);
+  const uint32_t H = (uint32_t)p.H, G = (uint32_t)p.G, L = (uint32_t)p.L;
+  const rsrc_t rx = make_rsrc(p.x + b * p.L * p.H * kP, L * H * kP * 4u);
+  const rsrc_t rb = make_rsrc(p.B + b * p.L * p.G * kN, L * G * kN * 4u);
+  const rsrc_t rdt = make_rsrc(p.dt + b * p.L * p.H, L * H * 4u);
+  const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
+  const int tid = threadIdx.x, row0 = 4 * (tid >> 4), col0 = 4 * (tid & 15);  // (p, n) tile
+  float S[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      S[r][c] = p.h0 ? p.h0[bh * kP * kN + (row0 + r) * kN + col0 + c] : 0.f;
+  for (int64_t c = 0; c < p.nc; ++c) {
+    const uint32_t t0 = (uint32_t)(c * kQ);
+    float *dst = p.states + (bh * p.nc + c) * (kP * kN);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) dst[(row0 + r) * kN + col0 + cc] = S[r][cc];
+    __syncthreads();  // the previous chunk's readers of sX/sB/cs are done
+    chunk_scalars(p, rdt, t0, L, H, (uint32_t)h, a_h, bias, cs);
+    load_tile(rx, t0, L, H, (uint32_t)h, sX);
+    load_tile(rb, t0, L, G, (uint32_t)g, sB);
+    __syncthreads();
+    // weight x_j by e^{Lam_end - Lam_j} delta_j in place (row j)
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int j = e >> 6, cc = e & 63;
+      sX[j * kLd + cc] *= cs.er[j] * cs.del[j];
+    }
+    __syncthreads();
+    float acc[4][4];
+    zero(acc);
+    mm(sX, 1, kLd, sB, kLd, 1, row0, col0, acc);  // X^T diag(w) B: A(p, j) = sX[j][p]
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) S[r][cc] = cs.elend * S[r][cc] + acc[r][cc];
+  }
+}
+
+// Backward: one workgroup per (b, h) walking the chunks from the last.
+__global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
+  __shared__ float sX[kQ * kLd], sDY[kQ * kLd], sB[kQ * kLd], sC[kQ * kLd];
+  __shared__ float sS[kP * kLd], sG[kP * kLd];
+  __shared__ float sW1[kQ * kLd], sW2[kQ * kLd], sT[kQ * kLd];
+  __shared__ float sPart[kQ * 17];
+  __shared__ float sRed[4 * 256 / 64];
+  __shared__ float sVec[6][kQ];  // q, r, w, v, dLam, (spare)
+  __shared__ ChunkScalars cs;
+
+  const int64_t bh = blockIdx.x, b = bh / p.H, h = bh % p.H;
+  const int64_t g = h / (p.H / p.G);
+  const uint32_t H = (uint32_t)p.H, G = (uint32_t)p.G, L = (uint32_t)p.L;
+  const rsrc_t rx = make_rsrc(p.x + b * p.L * p.H * kP, L * H * kP * 4u);
+  const rsrc_t rdy = make_rsrc(p.dout + b * p.L * p.H * kP, L * H * kP * 4u);
+  const rsrc_t rb = make_rsrc(p.B + b * p.L * p.G * kN, L * G * kN * 4u);
+  const rsrc_t rc = make_rsrc(p.C + b * p.L * p.G * kN, L * G * kN * 4u);
+  const rsrc_t rdt = make_rsrc(p.dt + b * p.L * p.H, L * H * 4u);
+  const rsrc_t rdx = make_rsrc(p.dx + b * p.L * p.H * kP, L * H * kP * 4u);
+  const rsrc_t rdb = make_rsrc(p.dBh + b * p.L * p.H * kN, L * H * kN * 4u);
+  const rsrc_t rdc = make_rsrc(p.dCh + b * p.L * p.H * kN, L * H * kN * 4u);
+  const rsrc_t rddt = make_rsrc(p.ddt + b * p.L * p.H, L * H * 4u);
+  const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
+  const float Dh = p.D ? p.D[h] : 0.f;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int row0 = 4 * (tid >> 4), col0 = 4 * (tid & 15);
+
+  // G = dfinal_state (or zero)
+  for (int e = tid; e < kP * kN; e += 256)
+    sG[(e >> 6) * kLd + (e & 63)] = p.dfin ? p.dfin[bh * kP * kN + e] : 0.f;
+  float accA = 0.f, accD = 0.f, accBias = 0.f;  // wave 0 / all threads' shares
+
+  for (int64_t c = p.nc - 1; c >= 0; --c) {
+    const uint32_t t0 = (uint32_t)(c * kQ);
+    __syncthreads();  // the previous chunk is done with every LDS array
+    chunk_scalars(p, rdt, t0, L, H, (uint32_t)h, a_h, bias, cs);
+    load_tile(rx, t0, L, H, (uint32_t)h, sX);
+    load_tile(rdy, t0, L, H, (uint32_t)h, sDY);
+    load_tile(rb, t0, L, G, (uint32_t)g, sB);
+    load_tile(rc, t0, L, G, (uint32_t)g, sC);
+    {
+      const float *src = p.states + (bh * p.nc + c) * (kP * kN);
+      for (int e = tid; e < kP * kN; e += 256) sS[(e >> 6) * kLd + (e & 63)] = src[e];
+    }
+    __syncthreads();
+
+    // dD share: sum of dout * x over the chunk
+    for (int e = tid; e < 64 * 64; e += 256) accD += sDY[(e >> 6) * kLd + (e & 63)] * sX[(e >> 6) * kLd + (e & 63)];
+
+    // CB_ij = C_i.B_j and DX_ij = dy_i.x_j, then the masked weights
+    {
+      float cb[4][4], dxm[4][4];
+      zero(cb);
+      zero(dxm);
+      mm(sC, kLd, 1, sB, 1, kLd, row0, col0, cb);    // A(i, n) = C[i][n], B(n, j) = B[j][n]
+      mm(sDY, kLd, 1, sX, 1, kLd, row0, col0, dxm);  // A(i, p) = dy[i][p], B(p, j) = x[j][p]
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int i = row0 + r, j = col0 + cc;
+          float w1 = 0.f, w2 = 0.f, t = 0.f;
+          if (j <= i) {
+            const float lij = __expf(cs.lam[i] - cs.lam[j]);
+            const float cbl = cb[r][cc] * lij;
+            t = cbl * dxm[r][cc];                    // d(y)/d(delta_j) weight, no delta
+            w1 = cbl * cs.del[j];
+            w2 = dxm[r][cc] * lij * cs.del[j];
+          }
+          sW1[i * kLd + j] = w1;
+          sW2[i * kLd + j] = w2;
+          sT[i * kLd + j] = t;
+        }
+    }
+    __syncthreads();
+    // q_j = sum_{i>=j} T_ij (direct intra gradient of delta_j);
+    // r_i = sum_{j<=i} T_ij delta_j (the part of dLam_i from the intra terms)
+    if (tid < 64) {
+      float q = 0.f;
+      for (int i = tid; i < 64; ++i) q += sT[i * kLd + tid];
+      sVec[0][tid] = q;
+    } else if (tid < 128) {
+      const int i = tid - 64;
+      float r = 0.f;
+      for (int j = 0; j <= i; ++j) r += sT[i * kLd + j] * cs.del[j];
+      sVec[1][i] = r;
+    }
+
+    // dx_j = sum_i W1_ij dy_i + delta_j e^{Lam_end-Lam_j} (B G^T)_j + D dy_j
+    {
+      float a1[4][4], a2[4][4];
+      zero(a1);
+      zero(a2);
+      mm(sW1, 1, kLd, sDY, kLd, 1, row0, col0, a1);  // A(j, i) = W1[i][j], B(i, p) = dy[i][p]
+      mm(sB, kLd, 1, sG, 1, kLd, row0, col0, a2);    // A(j, n) = B[j][n], B(n, p) = G[p][n]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = row0 + r;
+        const float f = cs.del[j] * cs.er[j];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int pp = col0 + cc;
+          const float v = a1[r][cc] + f * a2[r][cc] + Dh * sDY[j * kLd + pp];
+          st(rdx, t0 + j < L ? (((t0 + j) * H + (uint32_t)h) * kP + pp) * 4u : kOOB, v);
+        }
+      }
+    }
+    // dB_j = sum_i W2_ij C_i + delta_j e^{Lam_end-Lam_j} (X G)_j; w_j = (X G)_j . B_j
+    {
+      float a3[4][4], a4[4][4];
+      zero(a3);
+      zero(a4);
+      mm(sW2, 1, kLd, sC, kLd, 1, row0, col0, a3);   // A(j, i) = W2[i][j], B(i, n) = C[i][n]
+      mm(sX, kLd, 1, sG, kLd, 1, row0, col0, a4);    // A(j, p) = x[j][p], B(p, n) = G[p][n]
+      float wpart[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = row0 + r;
+        const float f = cs.del[j] * cs.er[j];
+        wpart[r] = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int n = col0 + cc;
+          st(rdb, t0 + j < L ? (((t0 + j) * H + (uint32_t)h) * kN + n) * 4u : kOOB,
+             a3[r][cc] + f * a4[r][cc]);
+          wpart[r] += a4[r][cc] * sB[j * kLd + n];
+        }
+        sPart[j * 17 + (tid & 15)] = wpart[r];
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float s = 0.f;
+      for (int k = 0; k < 16; ++k) s += sPart[tid * 17 + k];
+      sVec[2][tid] = s;  // w_j
+    }
+    __syncthreads();
+    // dC_i = sum_j W2_ij B_j + e^{Lam_i} (dy S)_i; v_i = (dy S)_i . C_i
+    {
+      float a5[4][4], a6[4][4];
+      zero(a5);
+      zero(a6);
+      mm(sW2, kLd, 1, sB, kLd, 1, row0, col0, a5);   // A(i, j) = W2[i][j], B(j, n) = B[j][n]
+      mm(sDY, kLd, 1, sS, kLd, 1, row0, col0, a6);   // A(i, p) = dy[i][p], B(p, n) = S[p][n]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = row0 + r;
+        float vpart = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int n = col0 + cc;
+          st(rdc, t0 + i < L ? (((t0 + i) * H + (uint32_t)h) * kN + n) * 4u : kOOB,
+             a5[r][cc] + cs.el[i] * a6[r][cc]);
+          vpart += a6[r][cc] * sC[i * kLd + n];
+        }
+        sPart[i * 17 + (tid & 15)] = vpart;
+      }
+    }
+    // <G, S> shares
+    {
+      float gs = 0.f;
+      for (int e = tid; e < kP * kN; e += 256) gs += sG[(e >> 6) * kLd + (e & 63)] * sS[(e >> 6) * kLd + (e & 63)];
+      gs = lane63(wave_scan(gs));
+      if (lane == 0) sRed[wv] = gs;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float s = 0.f;
+      for (int k = 0; k < 16; ++k) s += sPart[tid * 17 + k];
+      sVec[3][tid] = s;  // v_i
+    }
+    __syncthreads();
+
+    // token scalars (wave 0): dLam, the reverse cumsum, d delta, ddt, dA
+    if (tid < 64) {
+      const int k = tid;
+      const float dl = cs.del[k], er = cs.er[k];
+      const float w = sVec[2][k], U = dl * er * w;
+      float dlam = sVec[1][k] - dl * sVec[0][k] + cs.el[k] * sVec[3][k] - U;
+      const float gsum = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+      const float usum = lane63(wave_scan(U));
+      if (k == 63) dlam += cs.elend * gsum + usum;  // Lam_end = Lam_63
+      const float incl = wave_scan(dlam);
+      const float da = lane63(incl) - (incl - dlam);  // sum_{m>=k} dLam_m
+      const float ddelta = sVec[0][k] + er * w + a_h * da;
+      const float ddt = ddelta * cs.gfac[k];
+      st(rddt, t0 + k < L ? ((t0 + k) * H + (uint32_t)h) * 4u : kOOB, ddt);
+      accA += lane63(wave_scan(dl * da));
+      accBias += lane63(wave_scan(ddt));
+    }
+    __syncthreads();  // every reader of G and S above is done
+
+    // G <- e^{Lam_end} G + sum_i e^{Lam_i} dy_i (outer) C_i
+    {
+      float a7[4][4];
+      zero(a7);
+      // scale dy rows by e^{Lam_i} in place (dy is not read again this chunk)
+      for (int e = tid; e < 64 * 64; e += 256) sDY[(e >> 6) * kLd + (e & 63)] *= cs.el[e >> 6];
+      __syncthreads();
+      mm(sDY, 1, kLd, sC, kLd, 1, row0, col0, a7);   // A(p, i) = dy[i][p], B(i, n) = C[i][n]
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          float &gv = sG[(row0 + r) * kLd + col0 + cc];
+          gv = cs.elend * gv + a7[r][cc];
+        }
+    }
+  }
+  __syncthreads();
+  if (p.dh0)
+    for (int e = tid; e < kP * kN; e += 256) p.dh0[bh * kP * kN + e] = sG[(e >> 6) * kLd + (e & 63)];
+  // per-(b, h) partial sums: dA, ddt_bias from wave 0, dD from every thread
+  accD = lane63(wave_scan(accD));
+  __syncthreads();
+  if (lane == 0) sRed[wv] = accD;
+  __syncthreads();
+  if (tid == 0) {
+    p.part[bh * 4 + 0] = accA;
+    p.part[bh * 4 + 1] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+    p.part[bh * 4 + 2] = accBias;
+  }
+}
+
+// dB, dC: sum of the per-head values over the heads of each group; dA, dD,
+// ddt_bias: sums of the per-(b, h) partials over the batch.
+__global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdParams p) {
+  const int64_t hpg = p.H / p.G;
+  const int64_t n_bc = p.batch * p.L * p.G * kN;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < n_bc) {
+    const int64_t n = e % kN, rest = e / kN, gg = rest % p.G, bt = rest / p.G;
+    float sb = 0.f, sc = 0.f;
+    for (int64_t k = 0; k < hpg; ++k) {
+      const int64_t src = (bt * p.H + gg * hpg + k) * kN + n;
+      sb += p.dBh[src];
+      sc += p.dCh[src];
+    }
+    p.dB[e] = sb;
+    p.dC[e] = sc;
+  }
+  if (e < p.H) {
+    float sa = 0.f, sd = 0.f, sbias = 0.f;
+    for (int64_t bb = 0; bb < p.batch; ++bb) {
+      sa += p.part[(bb * p.H + e) * 4 + 0];
+      sd += p.part[(bb * p.H + e) * 4 + 1];
+      sbias += p.part[(bb * p.H + e) * 4 + 2];
+    }
+    p.dA[e] = sa;
+    if (p.dD) p.dD[e] = sd;
+    if (p.ddt_bias) p.ddt_bias[e] = sbias;
+  }
+}
+
+size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
+
+struct BwdWs {
+  size_t states, dbh, dch, part;
+  size_t total() const { return states + dbh + dch + part; }
+};
+
+BwdWs bwd_ws(const ssd_desc *d) {
+  const int64_t nc = (d->seqlen + kQ - 1) / kQ;
+  BwdWs w;
+  w.states = align_up((size_t)(d->batch * d->nheads * nc) * kP * kN * 4);
+  w.dbh = align_up((size_t)(d->batch * d->seqlen * d->nheads) * kN * 4);
+  w.dch = w.dbh;
+  w.part = align_up((size_t)(d->batch * d->nheads) * 4 * 4);
+  return w;
+}
+
+ssd_status check_bwd(const ssd_desc *d, int64_t chunk) {
+  if (!d) return SSD_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->seqlen < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+      d->ngroups < 1 || chunk < 1 || d->nheads % d->ngroups != 0)
+    return SSD_ERR_INVALID_ARG;
+  if (!(d->dt_min <= d->dt_max) || d->reserved != 0) return SSD_ERR_INVALID_ARG;
+  if (d->headdim != kP || d->dstate != kN || chunk != kQ) return SSD_ERR_UNSUPPORTED;
+  if (d->x_dtype != SSD_F32 || d->z || d->cu_seqlens) return SSD_ERR_UNSUPPORTED;
+  // 32-bit byte offsets within one batch row, 32-bit grid
+  if (d->seqlen * d->nheads * kP * 4 >= ((int64_t)1 << 31) || d->batch * d->nheads >= ((int64_t)1 << 31))
+    return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+bool aligned4(const void *ptr) { return ((uintptr_t)ptr & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_bwd_workspace_size(const ssd_desc *d, int64_t chunk, size_t *bytes) {
+  if (!bytes) return SSD_ERR_INVALID_ARG;
+  const ssd_status s = check_bwd(d, chunk);
+  if (s != SSD_OK) return s;
+  *bytes = bwd_ws(d).total();
+  return SSD_OK;
+}
+
+ssd_status ssd_bwd(const float *x, const float *dt, const float *A, const float *B,
+                   const float *C, const float *D, int64_t chunk, int dt_softplus,
+                   const float *dout, const float *dfinal_state, float *dx, float *ddt,
+                   float *dA, float *dB, float *dC, float *dD, float *ddt_bias,
+                   float *dinitial_state, void *stream, const ssd_desc *d) {
+  const ssd_status s = check_bwd(d, chunk);
+  if (s != SSD_OK) return s;
+  if (!x || !dt || !A || !B || !C || !dout || !dx || !ddt || !dA || !dB || !dC)
+    return SSD_ERR_INVALID_ARG;
+  if ((D && !dD) || (d->dt_bias && !ddt_bias)) return SSD_ERR_INVALID_ARG;
+  const void *ptrs[] = {x, dt, A, B, C, D, dout, dfinal_state, dx, ddt, dA, dB, dC, dD,
+                        ddt_bias, dinitial_state, d->dt_bias, d->initial_state, d->workspace};
+  for (const void *q : ptrs)
+    if (q && !aligned4(q)) return SSD_ERR_INVALID_ARG;
+  const BwdWs w = bwd_ws(d);
+  if (!d->workspace || d->workspace_bytes < w.total()) return SSD_ERR_WORKSPACE;
+
+  BwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x;
+  p.dt = dt;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.dt_bias = d->dt_bias;
+  p.h0 = d->initial_state;
+  p.dout = dout;
+  p.dfin = dfinal_state;
+  p.dx = dx;
+  p.ddt = ddt;
+  p.dA = dA;
+  p.dB = dB;
+  p.dC = dC;
+  p.dD = D ? dD : nullptr;
+  p.ddt_bias = d->dt_bias ? ddt_bias : nullptr;
+  p.dh0 = dinitial_state;
+  char *ws = static_cast<char *>(d->workspace);
+  p.states = reinterpret_cast<float *>(ws);
+  p.dBh = reinterpret_cast<float *>(ws + w.states);
+  p.dCh = reinterpret_cast<float *>(ws + w.states + w.dbh);
+  p.part = reinterpret_cast<float *>(ws + w.states + w.dbh + w.dch);
+  p.batch = d->batch;
+  p.L = d->seqlen;
+  p.H = d->nheads;
+  p.G = d->ngroups;
+  p.nc = (d->seqlen + kQ - 1) / kQ;
+  p.dt_min = d->dt_min;
+  p.dt_max = d->dt_max;
+  p.dt_softplus = dt_softplus ? 1 : 0;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned nbh = (unsigned)(d->batch * d->nheads);
+  hipLaunchKernelGGL(ssd_bwd_states_kernel, dim3(nbh), dim3(256), 0, st, p);
+  // the descriptor's measurement events bracket the main (chunk) kernel
+  if (d->ev_main_begin && hipEventRecord(static_cast<hipEvent_t>(d->ev_main_begin), st) != hipSuccess)
+    return SSD_ERR_LAUNCH;
+  hipLaunchKernelGGL(ssd_bwd_chunk_kernel, dim3(nbh), dim3(256), 0, st, p);
+  if (d->ev_main_end && hipEventRecord(static_cast<hipEvent_t>(d->ev_main_end), st) != hipSuccess)
+    return SSD_ERR_LAUNCH;
+  const int64_t n_bc = d->batch * d->seqlen * d->ngroups * kN;
+  const int64_t n_red = n_bc > d->nheads ? n_bc : d->nheads;
+  hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((unsigned)((n_red + 255) / 256)), dim3(256), 0,
+                     st, p);
+  return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -240,6 +240,51 @@ def test_misaligned_cu_seqlens(lib):
     assert _call(lib, d) == bnd.SSD_ERR_INVALID_ARG
 
 
+def _bwd(lib, desc, chunk=64, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, dout=FAKE, dfin=None, dx=FAKE,
+             ddt=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dbias=None, dh0=None)
+    a.update(kw)
+    return lib.ssd_bwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], chunk, 1, a["dout"],
+                       a["dfin"], a["dx"], a["ddt"], a["dA"], a["dB"], a["dC"], a["dD"],
+                       a["dbias"], a["dh0"], None, ctypes.byref(desc))
+
+
+def _bwd_desc(**kw):
+    d = _desc(N=64, **kw)
+    d.workspace, d.workspace_bytes = FAKE, 1 << 40
+    return d
+
+
+@pytest.mark.parametrize("kw", [dict(x=None), dict(dout=None), dict(dx=None), dict(dA=None),
+                                dict(D=FAKE), dict(dt=FAKE + 2)],
+                         ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_bwd_invalid_args(lib, kw):
+    assert _bwd(lib, _bwd_desc(), **kw) == bnd.SSD_ERR_INVALID_ARG
+
+
+def test_bwd_unsupported_and_workspace(lib):
+    assert _bwd(lib, _bwd_desc(), chunk=128) == bnd.SSD_ERR_UNSUPPORTED
+    d = _bwd_desc()
+    d.dstate = 128
+    assert _bwd(lib, d) == bnd.SSD_ERR_UNSUPPORTED
+    d = _bwd_desc()
+    d.z = FAKE
+    assert _bwd(lib, d) == bnd.SSD_ERR_UNSUPPORTED
+    d = _bwd_desc()
+    d.x_dtype = bnd.SSD_BF16
+    assert _bwd(lib, d) == bnd.SSD_ERR_UNSUPPORTED
+    d = _bwd_desc()
+    need = ctypes.c_size_t(0)
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(d), 64, ctypes.byref(need)) == bnd.SSD_OK
+    # states + per-head dB, dC + partials, each 256-byte aligned
+    nc = -(-d.seqlen // 64)
+    assert need.value >= 4 * (d.batch * d.nheads * nc * 64 * 64 + 2 * d.batch * d.seqlen * d.nheads * 64)
+    d.workspace_bytes = need.value - 1
+    assert _bwd(lib, d) == bnd.SSD_ERR_WORKSPACE
+    d.workspace = None
+    assert _bwd(lib, d) == bnd.SSD_ERR_WORKSPACE
+
+
 def test_product_path_does_not_touch_oracle():
     """The HIP path and its binding never import or load the oracle."""
     pkg = os.path.join(ROOT, "mamba_ssd_chunked_04_amd")
