@@ -24,7 +24,7 @@
 // Kernels: (1) ssd_bwd_states_kernel, one workgroup per (b, h), walks the
 // chunks forward and stores the state entering each; (2) ssd_bwd_chunk_kernel,
 // one workgroup per (b, h), walks the chunks backward carrying G in LDS, all
-// products as 4x4-per-thread fp32 tiles over LDS; (3) ssd_bwd_reduce_kernel
+// products as fp32 MFMA tiles (16x16x4) over LDS; (3) ssd_bwd_reduce_kernel
 // sums the per-head dB/dC over the heads of a group and dA, dD, ddt_bias over
 // the batch.
 #include <hip/hip_runtime.h>
@@ -42,6 +42,7 @@ constexpr int kLd = 65;                   // LDS row stride of the 64x64 tiles
 constexpr uint32_t kOOB = 0x80000000u;    // a byte offset past every range
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
@@ -95,15 +96,23 @@ struct ChunkScalars {
   float lend, elend;
 };
 
-// Discretise the chunk's steps and scan Lam; wave 0 computes, everyone reads
-// after the caller's barrier.  Tokens past the sequence end get delta = 0.
-__device__ __forceinline__ void chunk_scalars(const BwdParams &p, rsrc_t rdt, uint32_t t0,
-                                              uint32_t len, uint32_t H, uint32_t h, float a_h,
-                                              float bias, ChunkScalars &cs) {
+// Raw dt of token t0 + lane (wave 0; zero past the sequence end).
+__device__ __forceinline__ float fetch_dt(rsrc_t rdt, uint32_t t0, uint32_t len, uint32_t H,
+                                          uint32_t h) {
+  const uint32_t j = threadIdx.x & 63;
+  return ld(rdt, t0 + j < len ? ((t0 + j) * H + h) * 4u : kOOB);
+}
+
+// Discretise the chunk's steps (raw dt of token t0 + j in lane j of wave 0)
+// and scan Lam; wave 0 computes, everyone reads after the caller's barrier.
+// Tokens past the sequence end get delta = 0.
+__device__ __forceinline__ void chunk_scalars(const BwdParams &p, float dt_raw, uint32_t t0,
+                                              uint32_t len, float a_h, float bias,
+                                              ChunkScalars &cs) {
   if (threadIdx.x >= 64) return;
   const int j = threadIdx.x;
   const bool valid = t0 + j < len;
-  const float u = ld(rdt, valid ? ((t0 + j) * H + h) * 4u : kOOB) + bias;
+  const float u = dt_raw + bias;
   float sp = u, dsp = 1.f;
   if (p.dt_softplus) {
     const float e = __expf(-fabsf(u));
@@ -125,22 +134,38 @@ __device__ __forceinline__ void chunk_scalars(const BwdParams &p, rsrc_t rdt, ui
   }
 }
 
-// acc[r][c] += sum_k A(row0 + r, k) * B(k, col0 + c), k < 64, both in LDS:
-// A(i, k) = a[i * ars + k * aks], B(k, c) = b[k * bks + c * bcs].
+// Each thread owns 16 elements of a 64x64 product: rows row_of(r) (four
+// consecutive rows of its wave's 16) and columns col_of(c) (one per 16-column
+// tile), the accumulator layout of v_mfma_f32_16x16x4f32.
+__device__ __forceinline__ int row_of(int r) {
+  return 16 * (int)(threadIdx.x >> 6) + 4 * (int)((threadIdx.x & 63) >> 4) + r;
+}
+__device__ __forceinline__ int col_of(int c) { return 16 * c + (int)(threadIdx.x & 15); }
+
+// acc[r][c] += sum_{k<64} A(row_of(r), k) * B(k, col_of(c)), both in LDS:
+// A(i, k) = a[i * ars + k * aks], B(k, j) = b[k * bks + j * bcs].  Wave w
+// computes rows 16 w .. 16 w + 15 as four 16x16 tiles with fp32 MFMAs (lane
+// l supplies A(16 w + l % 16, k0 + l / 16) and B(k0 + l / 16, 16 c + l % 16)).
 __device__ __forceinline__ void mm(const float *a, int ars, int aks, const float *b, int bks,
-                                   int bcs, int row0, int col0, float (&acc)[4][4]) {
+                                   int bcs, float (&acc)[4][4]) {
+  const int lane = threadIdx.x & 63;
+  const int ai = 16 * (int)(threadIdx.x >> 6) + (lane & 15), kk = lane >> 4;
+  f32x4 d[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) d[c] = f32x4{acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
 #pragma unroll 4
-  for (int k = 0; k < 64; ++k) {
-    float av[4], bv[4];
+  for (int k0 = 0; k0 < 64; k0 += 4) {
+    const float av = a[ai * ars + (k0 + kk) * aks];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) av[r] = a[(row0 + r) * ars + k * aks];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) bv[c] = b[k * bks + (col0 + c) * bcs];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+    for (int c = 0; c < 4; ++c) {
+      const float bv = b[(k0 + kk) * bks + (16 * c + (lane & 15)) * bcs];
+      d[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, d[c], 0, 0, 0);
+    }
   }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r][c] = d[c][r];
 }
 
 __device__ __forceinline__ void zero(float (&acc)[4][4]) {
@@ -160,6 +185,49 @@ __device__ __forceinline__ void load_tile(rsrc_t r, uint32_t t0, uint32_t len, u
   }
 }
 
+// A 64x64 tile in flight in registers: thread t holds rows t/16 + 16 k
+// (k < 4), columns 4 (t % 16) .. +3, loaded 16 bytes at a time.
+struct Tile4 {
+  f32x4 v[4];
+};
+
+// Rows t0 .. t0+63 of one (b, h) of a [B, L, X, 64] tensor, zeros past the
+// sequence end (t0 = len fetches nothing).  The offsets are selects, never
+// branches: a load under a branch makes the compiler wait for every load in
+// flight where the paths merge.
+__device__ __forceinline__ void fetch_tile(rsrc_t r, uint32_t t0, uint32_t len, uint32_t X,
+                                           uint32_t slot, Tile4 &o) {
+  const uint32_t c4 = 4 * (threadIdx.x & 15);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t j = (threadIdx.x >> 4) + 16 * k;
+    const uint32_t off = t0 + j < len ? (((t0 + j) * X + slot) * 64 + c4) * 4u : kOOB;
+    o.v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+}
+
+// Dense 64x64 tile c of a [nc][64][64] array addressed by r (c = nc, past
+// the range, reads zeros).
+__device__ __forceinline__ void fetch_dense(rsrc_t r, uint32_t c, Tile4 &o) {
+  const uint32_t c4 = 4 * (threadIdx.x & 15);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t j = (threadIdx.x >> 4) + 16 * k;
+    o.v[k] = __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((c * 64 + j) * 64 + c4) * 4u, 0, 0));
+  }
+}
+
+__device__ __forceinline__ void stage_tile(const Tile4 &o, float *dst) {
+  const int c4 = 4 * (threadIdx.x & 15);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int j = (threadIdx.x >> 4) + 16 * k;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[j * kLd + c4 + e] = o.v[k][e];
+  }
+}
+
 // Forward pass that stores the state entering every chunk.
 __global__ __launch_bounds__(256) void ssd_bwd_states_kernel(BwdParams p) {
   __shared__ float sX[kQ * kLd], sB[kQ * kLd];
@@ -171,22 +239,22 @@ __global__ __launch_bounds__(256) void ssd_bwd_states_kernel(BwdParams p) {
   const rsrc_t rb = make_rsrc(p.B + b * p.L * p.G * kN, L * G * kN * 4u);
   const rsrc_t rdt = make_rsrc(p.dt + b * p.L * p.H, L * H * 4u);
   const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
-  const int tid = threadIdx.x, row0 = 4 * (tid >> 4), col0 = 4 * (tid & 15);  // (p, n) tile
-  float S[4][4];
+  const int tid = threadIdx.x;
+  float S[4][4];  // this thread's (p, n) = (row_of(r), col_of(c)) elements of the state
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      S[r][c] = p.h0 ? p.h0[bh * kP * kN + (row0 + r) * kN + col0 + c] : 0.f;
+      S[r][c] = p.h0 ? p.h0[bh * kP * kN + row_of(r) * kN + col_of(c)] : 0.f;
   for (int64_t c = 0; c < p.nc; ++c) {
     const uint32_t t0 = (uint32_t)(c * kQ);
     float *dst = p.states + (bh * p.nc + c) * (kP * kN);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) dst[(row0 + r) * kN + col0 + cc] = S[r][cc];
+      for (int cc = 0; cc < 4; ++cc) dst[row_of(r) * kN + col_of(cc)] = S[r][cc];
     __syncthreads();  // the previous chunk's readers of sX/sB/cs are done
-    chunk_scalars(p, rdt, t0, L, H, (uint32_t)h, a_h, bias, cs);
+    chunk_scalars(p, fetch_dt(rdt, t0, L, H, (uint32_t)h), t0, L, a_h, bias, cs);
     load_tile(rx, t0, L, H, (uint32_t)h, sX);
     load_tile(rb, t0, L, G, (uint32_t)g, sB);
     __syncthreads();
@@ -198,7 +266,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_states_kernel(BwdParams p) {
     __syncthreads();
     float acc[4][4];
     zero(acc);
-    mm(sX, 1, kLd, sB, kLd, 1, row0, col0, acc);  // X^T diag(w) B: A(p, j) = sX[j][p]
+    mm(sX, 1, kLd, sB, kLd, 1, acc);  // X^T diag(w) B: A(p, j) = sX[j][p]
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -210,8 +278,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_states_kernel(BwdParams p) {
 __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
   __shared__ float sX[kQ * kLd], sDY[kQ * kLd], sB[kQ * kLd], sC[kQ * kLd];
   __shared__ float sS[kP * kLd], sG[kP * kLd];
-  __shared__ float sW1[kQ * kLd], sW2[kQ * kLd], sT[kQ * kLd];
-  __shared__ float sPart[kQ * 17];
+  __shared__ float sW1[kQ * kLd], sW2[kQ * kLd];
+  __shared__ float sPart[kQ * 17], sRowPart[kQ * 17], sColPart[kQ * 17];
   __shared__ float sRed[4 * 256 / 64];
   __shared__ float sVec[6][kQ];  // q, r, w, v, dLam, (spare)
   __shared__ ChunkScalars cs;
@@ -231,25 +299,38 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
   const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
   const float Dh = p.D ? p.D[h] : 0.f;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int row0 = 4 * (tid >> 4), col0 = 4 * (tid & 15);
 
   // G = dfinal_state (or zero)
   for (int e = tid; e < kP * kN; e += 256)
     sG[(e >> 6) * kLd + (e & 63)] = p.dfin ? p.dfin[bh * kP * kN + e] : 0.f;
   float accA = 0.f, accD = 0.f, accBias = 0.f;  // wave 0 / all threads' shares
 
+  // the next chunk's tiles are in flight while the current one is computed
+  const rsrc_t rs = make_rsrc(p.states + bh * p.nc * (kP * kN), (uint32_t)(p.nc * kP * kN * 4));
+  Tile4 nx, ndy, nb, ncc, ns;
+  float ndt;
+  auto fetch = [&](int64_t cc) {  // cc = -1: nothing (zeros)
+    const uint32_t tb = cc >= 0 ? (uint32_t)cc * kQ : L;
+    const uint32_t cd = cc >= 0 ? (uint32_t)cc : (uint32_t)p.nc;
+    fetch_tile(rx, tb, L, H, (uint32_t)h, nx);
+    fetch_tile(rdy, tb, L, H, (uint32_t)h, ndy);
+    fetch_tile(rb, tb, L, G, (uint32_t)g, nb);
+    fetch_tile(rc, tb, L, G, (uint32_t)g, ncc);
+    fetch_dense(rs, cd, ns);
+    ndt = fetch_dt(rdt, tb, L, H, (uint32_t)h);
+  };
+  fetch(p.nc - 1);
+
   for (int64_t c = p.nc - 1; c >= 0; --c) {
     const uint32_t t0 = (uint32_t)(c * kQ);
     __syncthreads();  // the previous chunk is done with every LDS array
-    chunk_scalars(p, rdt, t0, L, H, (uint32_t)h, a_h, bias, cs);
-    load_tile(rx, t0, L, H, (uint32_t)h, sX);
-    load_tile(rdy, t0, L, H, (uint32_t)h, sDY);
-    load_tile(rb, t0, L, G, (uint32_t)g, sB);
-    load_tile(rc, t0, L, G, (uint32_t)g, sC);
-    {
-      const float *src = p.states + (bh * p.nc + c) * (kP * kN);
-      for (int e = tid; e < kP * kN; e += 256) sS[(e >> 6) * kLd + (e & 63)] = src[e];
-    }
+    chunk_scalars(p, ndt, t0, L, a_h, bias, cs);
+    stage_tile(nx, sX);
+    stage_tile(ndy, sDY);
+    stage_tile(nb, sB);
+    stage_tile(ncc, sC);
+    stage_tile(ns, sS);
+    fetch(c - 1);  // before the first chunk: zeros, unused
     __syncthreads();
 
     // dD share: sum of dout * x over the chunk
@@ -260,37 +341,47 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
       float cb[4][4], dxm[4][4];
       zero(cb);
       zero(dxm);
-      mm(sC, kLd, 1, sB, 1, kLd, row0, col0, cb);    // A(i, n) = C[i][n], B(n, j) = B[j][n]
-      mm(sDY, kLd, 1, sX, 1, kLd, row0, col0, dxm);  // A(i, p) = dy[i][p], B(p, j) = x[j][p]
+      mm(sC, kLd, 1, sB, 1, kLd, cb);    // A(i, n) = C[i][n], B(n, j) = B[j][n]
+      mm(sDY, kLd, 1, sX, 1, kLd, dxm);  // A(i, p) = dy[i][p], B(p, j) = x[j][p]
+      // T_ij = (C_i.B_j) e^{Lam_i-Lam_j} (dy_i.x_j): its column sums
+      // q_j = sum_{i>=j} T_ij (the direct intra gradient of delta_j) and row
+      // sums r_i = sum_{j<=i} T_ij delta_j (the intra part of dLam_i), summed
+      // per 4x4 tile here and across tiles below
+      float colp[4] = {0.f, 0.f, 0.f, 0.f}, rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          const int i = row0 + r, j = col0 + cc;
-          float w1 = 0.f, w2 = 0.f, t = 0.f;
-          if (j <= i) {
-            const float lij = __expf(cs.lam[i] - cs.lam[j]);
-            const float cbl = cb[r][cc] * lij;
-            t = cbl * dxm[r][cc];                    // d(y)/d(delta_j) weight, no delta
-            w1 = cbl * cs.del[j];
-            w2 = dxm[r][cc] * lij * cs.del[j];
-          }
+          const int i = row_of(r), j = col_of(cc);
+          // e^{Lam_i-Lam_j} for j <= i, e^{-inf} = 0 above the diagonal (a
+          // select, not a branch per element)
+          const float lij = __expf(j <= i ? cs.lam[i] - cs.lam[j] : -INFINITY);
+          const float cbl = cb[r][cc] * lij;
+          const float t = cbl * dxm[r][cc];
+          const float w1 = cbl * cs.del[j];
+          const float w2 = dxm[r][cc] * lij * cs.del[j];
           sW1[i * kLd + j] = w1;
           sW2[i * kLd + j] = w2;
-          sT[i * kLd + j] = t;
+          colp[cc] += t;
+          rowp[r] += t * cs.del[j];
         }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        sColPart[col_of(k) * 17 + (tid >> 4)] = colp[k];   // 16 row groups of 4
+        sRowPart[row_of(k) * 17 + (tid & 15)] = rowp[k];   // 16 column lanes
+      }
     }
     __syncthreads();
-    // q_j = sum_{i>=j} T_ij (direct intra gradient of delta_j);
-    // r_i = sum_{j<=i} T_ij delta_j (the part of dLam_i from the intra terms)
     if (tid < 64) {
       float q = 0.f;
-      for (int i = tid; i < 64; ++i) q += sT[i * kLd + tid];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) q += sColPart[tid * 17 + k];
       sVec[0][tid] = q;
     } else if (tid < 128) {
       const int i = tid - 64;
       float r = 0.f;
-      for (int j = 0; j <= i; ++j) r += sT[i * kLd + j] * cs.del[j];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) r += sRowPart[i * 17 + k];
       sVec[1][i] = r;
     }
 
@@ -299,15 +390,15 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
       float a1[4][4], a2[4][4];
       zero(a1);
       zero(a2);
-      mm(sW1, 1, kLd, sDY, kLd, 1, row0, col0, a1);  // A(j, i) = W1[i][j], B(i, p) = dy[i][p]
-      mm(sB, kLd, 1, sG, 1, kLd, row0, col0, a2);    // A(j, n) = B[j][n], B(n, p) = G[p][n]
+      mm(sW1, 1, kLd, sDY, kLd, 1, a1);  // A(j, i) = W1[i][j], B(i, p) = dy[i][p]
+      mm(sB, kLd, 1, sG, 1, kLd, a2);    // A(j, n) = B[j][n], B(n, p) = G[p][n]
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = row0 + r;
+        const int j = row_of(r);
         const float f = cs.del[j] * cs.er[j];
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          const int pp = col0 + cc;
+          const int pp = col_of(cc);
           const float v = a1[r][cc] + f * a2[r][cc] + Dh * sDY[j * kLd + pp];
           st(rdx, t0 + j < L ? (((t0 + j) * H + (uint32_t)h) * kP + pp) * 4u : kOOB, v);
         }
@@ -318,17 +409,17 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
       float a3[4][4], a4[4][4];
       zero(a3);
       zero(a4);
-      mm(sW2, 1, kLd, sC, kLd, 1, row0, col0, a3);   // A(j, i) = W2[i][j], B(i, n) = C[i][n]
-      mm(sX, kLd, 1, sG, kLd, 1, row0, col0, a4);    // A(j, p) = x[j][p], B(p, n) = G[p][n]
+      mm(sW2, 1, kLd, sC, kLd, 1, a3);   // A(j, i) = W2[i][j], B(i, n) = C[i][n]
+      mm(sX, kLd, 1, sG, kLd, 1, a4);    // A(j, p) = x[j][p], B(p, n) = G[p][n]
       float wpart[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = row0 + r;
+        const int j = row_of(r);
         const float f = cs.del[j] * cs.er[j];
         wpart[r] = 0.f;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          const int n = col0 + cc;
+          const int n = col_of(cc);
           st(rdb, t0 + j < L ? (((t0 + j) * H + (uint32_t)h) * kN + n) * 4u : kOOB,
              a3[r][cc] + f * a4[r][cc]);
           wpart[r] += a4[r][cc] * sB[j * kLd + n];
@@ -348,15 +439,15 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
       float a5[4][4], a6[4][4];
       zero(a5);
       zero(a6);
-      mm(sW2, kLd, 1, sB, kLd, 1, row0, col0, a5);   // A(i, j) = W2[i][j], B(j, n) = B[j][n]
-      mm(sDY, kLd, 1, sS, kLd, 1, row0, col0, a6);   // A(i, p) = dy[i][p], B(p, n) = S[p][n]
+      mm(sW2, kLd, 1, sB, kLd, 1, a5);   // A(i, j) = W2[i][j], B(j, n) = B[j][n]
+      mm(sDY, kLd, 1, sS, kLd, 1, a6);   // A(i, p) = dy[i][p], B(p, n) = S[p][n]
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = row0 + r;
+        const int i = row_of(r);
         float vpart = 0.f;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          const int n = col0 + cc;
+          const int n = col_of(cc);
           st(rdc, t0 + i < L ? (((t0 + i) * H + (uint32_t)h) * kN + n) * 4u : kOOB,
              a5[r][cc] + cs.el[i] * a6[r][cc]);
           vpart += a6[r][cc] * sC[i * kLd + n];
@@ -405,13 +496,13 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
       // scale dy rows by e^{Lam_i} in place (dy is not read again this chunk)
       for (int e = tid; e < 64 * 64; e += 256) sDY[(e >> 6) * kLd + (e & 63)] *= cs.el[e >> 6];
       __syncthreads();
-      mm(sDY, 1, kLd, sC, kLd, 1, row0, col0, a7);   // A(p, i) = dy[i][p], B(i, n) = C[i][n]
+      mm(sDY, 1, kLd, sC, kLd, 1, a7);   // A(p, i) = dy[i][p], B(i, n) = C[i][n]
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          float &gv = sG[(row0 + r) * kLd + col0 + cc];
+          float &gv = sG[row_of(r) * kLd + col_of(cc)];
           gv = cs.elend * gv + a7[r][cc];
         }
     }
