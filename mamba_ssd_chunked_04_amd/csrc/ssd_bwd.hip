@@ -175,16 +175,6 @@ __device__ __forceinline__ void zero(float (&acc)[4][4]) {
     for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
 }
 
-// Row-major [token][64] tile of one (b, h) chunk from a [B, L, X, 64] tensor
-// (X = H or G, column offset `slot`) into LDS, zeros past the sequence end.
-__device__ __forceinline__ void load_tile(rsrc_t r, uint32_t t0, uint32_t len, uint32_t X,
-                                          uint32_t slot, float *dst) {
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int j = e >> 6, c = e & 63;
-    dst[j * kLd + c] = ld(r, t0 + j < len ? (((t0 + j) * X + slot) * 64 + c) * 4u : kOOB);
-  }
-}
-
 // A 64x64 tile in flight in registers: thread t holds rows t/16 + 16 k
 // (k < 4), columns 4 (t % 16) .. +3, loaded 16 bytes at a time.
 struct Tile4 {
@@ -246,6 +236,16 @@ __global__ __launch_bounds__(256) void ssd_bwd_states_kernel(BwdParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       S[r][c] = p.h0 ? p.h0[bh * kP * kN + row_of(r) * kN + col_of(c)] : 0.f;
+  // the next chunk's x, B and dt are in flight while the current one is used
+  Tile4 nx, nb;
+  float ndt;
+  auto fetch = [&](int64_t cc) {  // cc = nc: nothing (zeros)
+    const uint32_t tb = cc < p.nc ? (uint32_t)cc * kQ : L;
+    fetch_tile(rx, tb, L, H, (uint32_t)h, nx);
+    fetch_tile(rb, tb, L, G, (uint32_t)g, nb);
+    ndt = fetch_dt(rdt, tb, L, H, (uint32_t)h);
+  };
+  fetch(0);
   for (int64_t c = 0; c < p.nc; ++c) {
     const uint32_t t0 = (uint32_t)(c * kQ);
     float *dst = p.states + (bh * p.nc + c) * (kP * kN);
@@ -254,9 +254,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_states_kernel(BwdParams p) {
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) dst[row_of(r) * kN + col_of(cc)] = S[r][cc];
     __syncthreads();  // the previous chunk's readers of sX/sB/cs are done
-    chunk_scalars(p, fetch_dt(rdt, t0, L, H, (uint32_t)h), t0, L, a_h, bias, cs);
-    load_tile(rx, t0, L, H, (uint32_t)h, sX);
-    load_tile(rb, t0, L, G, (uint32_t)g, sB);
+    chunk_scalars(p, ndt, t0, L, a_h, bias, cs);
+    stage_tile(nx, sX);
+    stage_tile(nb, sB);
+    fetch(c + 1);
     __syncthreads();
     // weight x_j by e^{Lam_end - Lam_j} delta_j in place (row j)
     for (int e = tid; e < 64 * 64; e += 256) {
