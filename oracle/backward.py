@@ -11,8 +11,8 @@ D, dt_bias, the initial state) for contiguous P = N = chunk = 64 in FP32.
 ssd_grads writes the recurrence once more, here in plain PyTorch fp64 ops
 (a loop over tokens, vectorised over batch, heads and the state), and takes
 its gradients with torch.autograd: the definition of the backward, with no
-chunking.  The gate z is not part of this backward (it is applied outside,
-as an elementwise op).  Pinned by central finite differences of the fp64 C
+chunking.  With z the output is gated as in the forward, out = y * silu(z),
+and dz is returned.  Pinned by central finite differences of the fp64 C
 recurrence in tests/test_oracle_backward.py.
 
 Readings (listed again in the design doc): the gradient of the clamp is zero
@@ -35,18 +35,19 @@ def _t(a, torch):
     return torch.tensor(np.asarray(a, dtype=np.float64))
 
 
-def ssd_grads(x, dt, A, B, C, dout, D=None, dt_bias=None, initial_states=None,
+def ssd_grads(x, dt, A, B, C, dout, D=None, z=None, dt_bias=None, initial_states=None,
               dfinal_state=None, dt_softplus: bool = False,
               dt_limit: Tuple[float, float] = (0.0, math.inf)) -> Dict[str, Optional[np.ndarray]]:
     """Gradients of L = <dout, out> + <dfinal_state, final_state>.
 
     x [B,L,H,P], dt [B,L,H], A [H], B/C [B,L,G,N], dout [B,L,H,P],
-    D [H], dt_bias [H], initial_states [B,H,P,N], dfinal_state [B,H,P,N]
-    (optional ones may be None).  Returns a dict of fp64 arrays: dx, ddt, dA,
-    dB, dC and, for the optional inputs given, dD, ddt_bias, dinitial_states.
+    D [H], z [B,L,H,P], dt_bias [H], initial_states [B,H,P,N], dfinal_state
+    [B,H,P,N] (optional ones may be None).  Returns a dict of fp64 arrays: dx,
+    ddt, dA, dB, dC and, for the optional inputs given, dD, dz, ddt_bias,
+    dinitial_states.
     """
     import torch
-    xs = {"x": x, "dt": dt, "A": A, "B": B, "C": C, "D": D, "dt_bias": dt_bias,
+    xs = {"x": x, "dt": dt, "A": A, "B": B, "C": C, "D": D, "z": z, "dt_bias": dt_bias,
           "initial_states": initial_states}
     v = {k: _t(a, torch) for k, a in xs.items()}
     for k, a in v.items():
@@ -73,10 +74,12 @@ def ssd_grads(x, dt, A, B, C, dout, D=None, dt_bias=None, initial_states=None,
             y = y + v["D"][None, :, None] * v["x"][:, t]
         ys.append(y)
     out = torch.stack(ys, dim=1)                                      # [B,L,H,P]
+    if v["z"] is not None:
+        out = out * (v["z"] * torch.sigmoid(v["z"]))
     loss = (out * _t(dout, torch)).sum()
     if dfinal_state is not None:
         loss = loss + (S * _t(dfinal_state, torch)).sum()
     loss.backward()
-    names = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD",
+    names = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
              "dt_bias": "ddt_bias", "initial_states": "dinitial_states"}
     return {names[k]: (None if a is None else a.grad.numpy()) for k, a in v.items()}

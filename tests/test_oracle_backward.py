@@ -5,7 +5,8 @@ fp64.  It is pinned against central finite differences of the forward
 computed by the separate fp64 C recurrence (ssd_recurrence), element by
 element for every input, and against the A = 0 closed form of dx and dB.
 A dropped decay term, a wrong group map, a missing softplus derivative or
-clamp mask, or a final-state gradient not reaching the inputs each fails.
+clamp mask, a gate derivative taken as sigmoid, or a final-state gradient
+not reaching the inputs each fails.
 """
 import math
 
@@ -21,6 +22,7 @@ def _case(seed, Bsz=1, L=7, H=2, P=3, N=2, G=1, opts=True):
          "A": -r.random(H) - 0.2, "B": r.standard_normal((Bsz, L, G, N)),
          "C": r.standard_normal((Bsz, L, G, N)),
          "D": r.standard_normal(H) if opts else None,
+         "z": r.standard_normal((Bsz, L, H, P)) if opts else None,
          "dt_bias": r.random(H) - 0.5 if opts else None,
          "initial_states": 0.3 * r.standard_normal((Bsz, H, P, N)) if opts else None}
     dout = r.standard_normal((Bsz, L, H, P))
@@ -29,7 +31,7 @@ def _case(seed, Bsz=1, L=7, H=2, P=3, N=2, G=1, opts=True):
 
 
 def _loss(d, dout, dfin, softplus, limit):
-    out, fin = ssd_recurrence(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"],
+    out, fin = ssd_recurrence(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
                               dt_bias=d["dt_bias"], initial_states=d["initial_states"],
                               dt_softplus=softplus, dt_limit=limit)
     val = float(np.sum(out * dout))
@@ -38,7 +40,7 @@ def _loss(d, dout, dfin, softplus, limit):
     return val
 
 
-NAMES = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD",
+NAMES = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
          "dt_bias": "ddt_bias", "initial_states": "dinitial_states"}
 
 
@@ -51,9 +53,9 @@ def test_matches_finite_differences(cfg):
     cfg = dict(cfg)
     softplus, limit = cfg.pop("softplus"), cfg.pop("limit")
     d, dout, dfin = _case(**cfg)
-    g = ssd_grads(d["x"], d["dt"], d["A"], d["B"], d["C"], dout, D=d["D"], dt_bias=d["dt_bias"],
-                  initial_states=d["initial_states"], dfinal_state=dfin, dt_softplus=softplus,
-                  dt_limit=limit)
+    g = ssd_grads(d["x"], d["dt"], d["A"], d["B"], d["C"], dout, D=d["D"], z=d["z"],
+                  dt_bias=d["dt_bias"], initial_states=d["initial_states"], dfinal_state=dfin,
+                  dt_softplus=softplus, dt_limit=limit)
     eps = 1e-6
     for k, arr in d.items():
         if arr is None:
@@ -75,9 +77,9 @@ def test_matches_finite_differences(cfg):
 def test_clamped_steps_have_no_dt_gradient():
     d, dout, dfin = _case(5, L=9)
     limit = (0.45, 0.75)
-    g = ssd_grads(d["x"], d["dt"], d["A"], d["B"], d["C"], dout, D=d["D"], dt_bias=d["dt_bias"],
-                  initial_states=d["initial_states"], dfinal_state=dfin, dt_softplus=True,
-                  dt_limit=limit)
+    g = ssd_grads(d["x"], d["dt"], d["A"], d["B"], d["C"], dout, D=d["D"], z=d["z"],
+                  dt_bias=d["dt_bias"], initial_states=d["initial_states"], dfinal_state=dfin,
+                  dt_softplus=True, dt_limit=limit)
     u = d["dt"] + d["dt_bias"][None, None, :]
     sp = np.log1p(np.exp(u))
     clamped = (sp < limit[0]) | (sp > limit[1])
