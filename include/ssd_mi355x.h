@@ -162,18 +162,20 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A,
 ssd_status ssd_bwd_workspace_size(const ssd_desc *d, int64_t chunk, size_t *bytes);
 
 /* SSD backward: gradients of L = <dout, out> + <dfinal_state, final_state>
- * for the forward ssd_fwd computes (no z gate), in fp32.  The scope is the
+ * for the forward ssd_fwd computes, in fp32.  The scope is the
  * one the page "Mamba-2 SSD for Ascend NPU" gives its first backward
  * ("AscendC training", "Limitations and roadmap"): contiguous
  * P = N = chunk = 64, fp32 storage.  The descriptor gives the shape,
- * dt_bias, dt_limit, initial_state and the workspace (ssd_bwd_workspace_size
- * bytes, no initialisation needed); z and cu_seqlens must be NULL, x_dtype
- * SSD_F32 (mma is ignored: all arithmetic is fp32).
+ * dt_bias, dt_limit, initial_state, the gate z (fp32; out = y * silu(z))
+ * and the workspace (ssd_bwd_workspace_size bytes, no initialisation
+ * needed); cu_seqlens must be NULL and x_dtype SSD_F32 (mma is ignored: all
+ * arithmetic is fp32).
  *   inputs  x, dout [B,L,H,P]; dt [B,L,H]; A [H]; B, C [B,L,G,N]; D [H] or
  *           NULL; dfinal_state [B,H,P,N] or NULL (zero)
  *   outputs dx [B,L,H,P]; ddt [B,L,H]; dA [H]; dB, dC [B,L,G,N]; dD [H]
- *           (required when D is given); ddt_bias [H] (required when
- *           dt_bias is given); dinitial_state [B,H,P,N] or NULL (not written)
+ *           (required when D is given); dz [B,L,H,P] (required when z is
+ *           given); ddt_bias [H] (required when dt_bias is given);
+ *           dinitial_state [B,H,P,N] or NULL (not written)
  * Every output is overwritten.  dA, dD and ddt_bias sum over the batch, dB
  * and dC over the heads of each group.  Results are deterministic.  The
  * descriptor's ev_main_begin/ev_main_end bracket the main backward kernel.
@@ -184,8 +186,9 @@ ssd_status ssd_bwd_workspace_size(const ssd_desc *d, int64_t chunk, size_t *byte
 ssd_status ssd_bwd(const float *x, const float *dt, const float *A, const float *B,
                    const float *C, const float *D, int64_t chunk, int dt_softplus,
                    const float *dout, const float *dfinal_state, float *dx, float *ddt,
-                   float *dA, float *dB, float *dC, float *dD, float *ddt_bias,
-                   float *dinitial_state, void *stream, const ssd_desc *d);
+                   float *dA, float *dB, float *dC, float *dD, float *dz,
+                   float *ddt_bias, float *dinitial_state, void *stream,
+                   const ssd_desc *d);
 
 /* Gated grouped RMSNorm, the operator that closes the SSD chain (page
  * "ops-transformer MambaV2 算子套件", §4.6, mamba2_rmsnormgated):

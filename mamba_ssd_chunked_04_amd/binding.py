@@ -72,7 +72,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ssd_rmsnorm_gated.restype = c_int
     lib.ssd_bwd_workspace_size.argtypes = [dp, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.ssd_bwd_workspace_size.restype = c_int
-    lib.ssd_bwd.argtypes = [vp] * 6 + [i64, c_int] + [vp] * 10 + [vp, dp]
+    lib.ssd_bwd.argtypes = [vp] * 6 + [i64, c_int] + [vp] * 11 + [vp, dp]
     lib.ssd_bwd.restype = c_int
     lib.ssd_causal_conv1d.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, c_int, vp, vp, vp]
     lib.ssd_causal_conv1d.restype = c_int
@@ -339,13 +339,13 @@ class SsdBwdCall:
         _raise_for(st, "ssd_bwd")
 
 
-def prepare_bwd(x, dt, A, B, C, dout, chunk_size: int = 64, D=None, dt_bias=None,
+def prepare_bwd(x, dt, A, B, C, dout, chunk_size: int = 64, D=None, z=None, dt_bias=None,
                 initial_states=None, dfinal_state=None, dt_softplus: bool = False,
                 dt_limit: Tuple[float, float] = (0.0, math.inf)):
     """Validate, allocate the gradients and the workspace, build an SsdBwdCall.
 
-    fp32 tensors in the ssd_fwd layouts (no z gate).  ``call.grads`` holds dx,
-    ddt, dA, dB, dC and, for the optional inputs given, dD, ddt_bias,
+    fp32 tensors in the ssd_fwd layouts.  ``call.grads`` holds dx, ddt, dA,
+    dB, dC and, for the optional inputs given, dD, dz, ddt_bias,
     dinitial_states.
     """
     import torch
@@ -357,18 +357,20 @@ def prepare_bwd(x, dt, A, B, C, dout, chunk_size: int = 64, D=None, dt_bias=None
     G, N = B.shape[2], B.shape[3]
     shapes = (("dt", dt, (Bsz, L, H)), ("A", A, (H,)), ("B", B, (Bsz, L, G, N)),
               ("C", C, (Bsz, L, G, N)), ("dout", dout, (Bsz, L, H, P)), ("D", D, (H,)),
+              ("z", z, (Bsz, L, H, P)),
               ("dt_bias", dt_bias, (H,)), ("initial_states", initial_states, (Bsz, H, P, N)),
               ("dfinal_state", dfinal_state, (Bsz, H, P, N)))
     for name, t, shp in shapes:
         if t is not None and tuple(t.shape) != shp:
             raise ValueError(f"{name} must have shape {shp}")
-    for t in (x, dt, A, B, C, dout, D, dt_bias, initial_states, dfinal_state):
+    for t in (x, dt, A, B, C, dout, D, z, dt_bias, initial_states, dfinal_state):
         if t is not None and (t.dtype != torch.float32 or t.device != dev or not t.is_contiguous()):
             raise ValueError("all tensors must be contiguous float32 on the same GPU")
     desc = make_desc(Bsz, L, H, P, N, G)
     desc.mma = SSD_MMA_F32
     desc.dt_min, desc.dt_max = float(dt_limit[0]), float(dt_limit[1])
     desc.dt_bias, desc.initial_state = _ptr(dt_bias), _ptr(initial_states)
+    desc.z = _ptr(z)
     n = ctypes.c_size_t(0)
     _raise_for(load_library().ssd_bwd_workspace_size(ctypes.byref(desc), int(chunk_size),
                                                      ctypes.byref(n)), "ssd_bwd_workspace_size")
@@ -377,22 +379,23 @@ def prepare_bwd(x, dt, A, B, C, dout, chunk_size: int = 64, D=None, dt_bias=None
     e = lambda *s: torch.empty(*s, device=dev, dtype=torch.float32)
     grads = {"dx": e(Bsz, L, H, P), "ddt": e(Bsz, L, H), "dA": e(H), "dB": e(Bsz, L, G, N),
              "dC": e(Bsz, L, G, N), "dD": e(H) if D is not None else None,
+             "dz": e(Bsz, L, H, P) if z is not None else None,
              "ddt_bias": e(H) if dt_bias is not None else None,
              "dinitial_states": e(Bsz, H, P, N) if initial_states is not None else None}
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk_size),
             int(bool(dt_softplus)), _ptr(dout), _ptr(dfinal_state),
-            *(_ptr(grads[k]) for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "ddt_bias",
+            *(_ptr(grads[k]) for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "dz", "ddt_bias",
                                        "dinitial_states")))
-    keep = (x, dt, A, B, C, dout, D, dt_bias, initial_states, dfinal_state, ws)
+    keep = (x, dt, A, B, C, dout, D, z, dt_bias, initial_states, dfinal_state, ws)
     return SsdBwdCall(args, desc, keep, grads)
 
 
-def ssd_bwd(x, dt, A, B, C, dout, chunk_size: int = 64, D=None, dt_bias=None,
+def ssd_bwd(x, dt, A, B, C, dout, chunk_size: int = 64, D=None, z=None, dt_bias=None,
             initial_states=None, dfinal_state=None, dt_softplus: bool = False,
             dt_limit: Tuple[float, float] = (0.0, math.inf)):
     """SSD backward on the current torch stream; returns the dict of gradients."""
     import torch
-    call = prepare_bwd(x, dt, A, B, C, dout, chunk_size, D=D, dt_bias=dt_bias,
+    call = prepare_bwd(x, dt, A, B, C, dout, chunk_size, D=D, z=z, dt_bias=dt_bias,
                        initial_states=initial_states, dfinal_state=dfinal_state,
                        dt_softplus=dt_softplus, dt_limit=dt_limit)
     with torch.cuda.device(x.device):

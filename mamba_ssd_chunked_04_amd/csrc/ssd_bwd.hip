@@ -5,7 +5,8 @@
 // its chunked form) with the tensor semantics of page "Mamba-2 SSD for Ascend
 // NPU", "Implementation"; that page's "AscendC training" section and
 // "Limitations and roadmap" scope a first backward to contiguous
-// P = N = chunk = 64 in FP32, which is the scope here (no z gate).
+// P = N = chunk = 64 in FP32, which is the scope here, with the optional z
+// gate of the forward (out = y silu(z)) and its gradient.
 //
 // Per chunk, with delta_j the discretised step, Lam the in-chunk inclusive
 // prefix of delta*A (natural log units), S the state entering the chunk and
@@ -80,8 +81,8 @@ __device__ __forceinline__ float lane63(float v) {
 }
 
 struct BwdParams {
-  const float *x, *dt, *A, *B, *C, *D, *dt_bias, *h0, *dout, *dfin;
-  float *dx, *ddt, *dA, *dB, *dC, *dD, *ddt_bias, *dh0;
+  const float *x, *dt, *A, *B, *C, *D, *z, *dt_bias, *h0, *dout, *dfin;
+  float *dx, *ddt, *dA, *dB, *dC, *dD, *dz, *ddt_bias, *dh0;
   float *states;        // [B*H][nc][P][N]: state entering each chunk
   float *dBh, *dCh;     // [B][L][H][N]: per-head dB, dC
   float *part;          // [B*H][4]: per-(b,h) dA, dD, ddt_bias partial sums
@@ -89,6 +90,9 @@ struct BwdParams {
   float dt_min, dt_max;
   int dt_softplus;
 };
+
+// silu(v) = v sigmoid(v) and its derivative sigmoid(v) (1 + v (1 - sigmoid(v))).
+__device__ __forceinline__ float sigm(float v) { return 1.f / (1.f + __expf(-v)); }
 
 // Per-chunk scalars in LDS.
 struct ChunkScalars {
@@ -297,6 +301,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
   const rsrc_t rdb = make_rsrc(p.dBh + b * p.L * p.H * kN, L * H * kN * 4u);
   const rsrc_t rdc = make_rsrc(p.dCh + b * p.L * p.H * kN, L * H * kN * 4u);
   const rsrc_t rddt = make_rsrc(p.ddt + b * p.L * p.H, L * H * 4u);
+  // the gate (optional): dy = dout silu(z), dz = dout silu'(z) y_pre
+  const bool gated = p.z != nullptr;
+  const rsrc_t rz = make_rsrc(gated ? p.z + b * p.L * p.H * kP : nullptr, gated ? L * H * kP * 4u : 0u);
+  const rsrc_t rdz = make_rsrc(gated ? p.dz + b * p.L * p.H * kP : nullptr, gated ? L * H * kP * 4u : 0u);
   const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
   const float Dh = p.D ? p.D[h] : 0.f;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -308,7 +316,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
 
   // the next chunk's tiles are in flight while the current one is computed
   const rsrc_t rs = make_rsrc(p.states + bh * p.nc * (kP * kN), (uint32_t)(p.nc * kP * kN * 4));
-  Tile4 nx, ndy, nb, ncc, ns;
+  Tile4 nx, ndy, nb, ncc, ns, nz;
   float ndt;
   auto fetch = [&](int64_t cc) {  // cc = -1: nothing (zeros)
     const uint32_t tb = cc >= 0 ? (uint32_t)cc * kQ : L;
@@ -319,6 +327,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
     fetch_tile(rc, tb, L, G, (uint32_t)g, ncc);
     fetch_dense(rs, cd, ns);
     ndt = fetch_dt(rdt, tb, L, H, (uint32_t)h);
+    fetch_tile(rz, tb, L, H, (uint32_t)h, nz);  // zeros without a gate
   };
   fetch(p.nc - 1);
 
@@ -327,6 +336,19 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
     __syncthreads();  // the previous chunk is done with every LDS array
     chunk_scalars(p, ndt, t0, L, a_h, bias, cs);
     stage_tile(nx, sX);
+    // dy = dout silu(z) into LDS; gz = dout silu'(z) stays in registers for
+    // dz, in the same (fetch) element order
+    f32x4 gz[4];
+    if (gated) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float zz = nz.v[k][e], sg = sigm(zz), dout = ndy.v[k][e];
+          ndy.v[k][e] = dout * zz * sg;
+          gz[k][e] = dout * sg * (1.f + zz * (1.f - sg));
+        }
+    }
     stage_tile(ndy, sDY);
     stage_tile(nb, sB);
     stage_tile(ncc, sC);
@@ -403,6 +425,39 @@ __global__ __launch_bounds__(256) void ssd_bwd_chunk_kernel(BwdParams p) {
           const float v = a1[r][cc] + f * a2[r][cc] + Dh * sDY[j * kLd + pp];
           st(rdx, t0 + j < L ? (((t0 + j) * H + (uint32_t)h) * kP + pp) * 4u : kOOB, v);
         }
+      }
+    }
+    // the gate gradient: y_pre = W1 x + e^{Lam} C S^T + D x, recomputed, and
+    // dz = dout silu'(z) y_pre; y_pre goes through sW1 (no longer read) to
+    // the fetch element order of gz
+    if (gated) {
+      float a8[4][4];
+      zero(a8);
+      mm(sW1, kLd, 1, sX, kLd, 1, a8);   // A(i, j) = W1[i][j], B(j, p) = x[j][p]
+      float a9[4][4];
+      zero(a9);
+      mm(sC, kLd, 1, sS, 1, kLd, a9);    // A(i, n) = C[i][n], B(n, p) = S[p][n]
+      __syncthreads();                   // every wave is done reading sW1
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = row_of(r);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int pp = col_of(cc);
+          sW1[i * kLd + pp] = a8[r][cc] + cs.el[i] * a9[r][cc] + Dh * sX[i * kLd + pp];
+        }
+      }
+      __syncthreads();
+      const uint32_t c4 = 4 * (tid & 15);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t j = (tid >> 4) + 16 * k;
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = gz[k][e] * sW1[j * kLd + c4 + e];
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, o), rdz,
+            t0 + j < L ? (((t0 + j) * H + (uint32_t)h) * kP + c4) * 4u : kOOB, 0, 0);
       }
     }
     // dB_j = sum_i W2_ij C_i + delta_j e^{Lam_end-Lam_j} (X G)_j; w_j = (X G)_j . B_j
@@ -577,7 +632,8 @@ ssd_status check_bwd(const ssd_desc *d, int64_t chunk) {
     return SSD_ERR_INVALID_ARG;
   if (!(d->dt_min <= d->dt_max) || d->reserved != 0) return SSD_ERR_INVALID_ARG;
   if (d->headdim != kP || d->dstate != kN || chunk != kQ) return SSD_ERR_UNSUPPORTED;
-  if (d->x_dtype != SSD_F32 || d->z || d->cu_seqlens) return SSD_ERR_UNSUPPORTED;
+  if (d->x_dtype != SSD_F32 || (d->z && d->z_dtype != SSD_F32) || d->cu_seqlens)
+    return SSD_ERR_UNSUPPORTED;
   // 32-bit byte offsets within one batch row, 32-bit grid
   if (d->seqlen * d->nheads * kP * 4 >= ((int64_t)1 << 31) || d->batch * d->nheads >= ((int64_t)1 << 31))
     return SSD_ERR_UNSUPPORTED;
@@ -601,15 +657,16 @@ ssd_status ssd_bwd_workspace_size(const ssd_desc *d, int64_t chunk, size_t *byte
 ssd_status ssd_bwd(const float *x, const float *dt, const float *A, const float *B,
                    const float *C, const float *D, int64_t chunk, int dt_softplus,
                    const float *dout, const float *dfinal_state, float *dx, float *ddt,
-                   float *dA, float *dB, float *dC, float *dD, float *ddt_bias,
+                   float *dA, float *dB, float *dC, float *dD, float *dz, float *ddt_bias,
                    float *dinitial_state, void *stream, const ssd_desc *d) {
   const ssd_status s = check_bwd(d, chunk);
   if (s != SSD_OK) return s;
   if (!x || !dt || !A || !B || !C || !dout || !dx || !ddt || !dA || !dB || !dC)
     return SSD_ERR_INVALID_ARG;
-  if ((D && !dD) || (d->dt_bias && !ddt_bias)) return SSD_ERR_INVALID_ARG;
+  if ((D && !dD) || (d->dt_bias && !ddt_bias) || (d->z && !dz)) return SSD_ERR_INVALID_ARG;
   const void *ptrs[] = {x, dt, A, B, C, D, dout, dfinal_state, dx, ddt, dA, dB, dC, dD,
-                        ddt_bias, dinitial_state, d->dt_bias, d->initial_state, d->workspace};
+                        dz, ddt_bias, dinitial_state, d->dt_bias, d->initial_state, d->z,
+                        d->workspace};
   for (const void *q : ptrs)
     if (q && !aligned4(q)) return SSD_ERR_INVALID_ARG;
   const BwdWs w = bwd_ws(d);
@@ -635,6 +692,8 @@ ssd_status ssd_bwd(const float *x, const float *dt, const float *A, const float 
   p.dD = D ? dD : nullptr;
   p.ddt_bias = d->dt_bias ? ddt_bias : nullptr;
   p.dh0 = dinitial_state;
+  p.z = static_cast<const float *>(d->z);
+  p.dz = d->z ? dz : nullptr;
   char *ws = static_cast<char *>(d->workspace);
   p.states = reinterpret_cast<float *>(ws);
   p.dBh = reinterpret_cast<float *>(ws + w.states);

@@ -242,10 +242,10 @@ def test_misaligned_cu_seqlens(lib):
 
 def _bwd(lib, desc, chunk=64, **kw):
     a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, dout=FAKE, dfin=None, dx=FAKE,
-             ddt=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dbias=None, dh0=None)
+             ddt=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, dbias=None, dh0=None)
     a.update(kw)
     return lib.ssd_bwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], chunk, 1, a["dout"],
-                       a["dfin"], a["dx"], a["ddt"], a["dA"], a["dB"], a["dC"], a["dD"],
+                       a["dfin"], a["dx"], a["ddt"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
                        a["dbias"], a["dh0"], None, ctypes.byref(desc))
 
 
@@ -268,8 +268,11 @@ def test_bwd_unsupported_and_workspace(lib):
     d.dstate = 128
     assert _bwd(lib, d) == bnd.SSD_ERR_UNSUPPORTED
     d = _bwd_desc()
-    d.z = FAKE
+    d.z, d.z_dtype = FAKE, bnd.SSD_BF16
     assert _bwd(lib, d) == bnd.SSD_ERR_UNSUPPORTED
+    d = _bwd_desc()
+    d.z = FAKE                                   # a gate needs its gradient output
+    assert _bwd(lib, d) == bnd.SSD_ERR_INVALID_ARG
     d = _bwd_desc()
     d.x_dtype = bnd.SSD_BF16
     assert _bwd(lib, d) == bnd.SSD_ERR_UNSUPPORTED

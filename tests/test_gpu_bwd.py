@@ -1,8 +1,9 @@
 """GPU parity of the SSD backward (ssd_bwd through the C ABI) against the fp64
 autograd oracle.
 
-Scope of the backward: P = N = chunk = 64, fp32 (page "Mamba-2 SSD for
-Ascend NPU", "AscendC training" and "Limitations and roadmap").  Bar per
+Scope of the backward: P = N = chunk = 64, fp32, with the optional z gate
+(page "Mamba-2 SSD for Ascend NPU", "AscendC training" and "Limitations and
+roadmap").  Bar per
 gradient tensor: max|gpu - oracle| <= 1e-4 * max|oracle|, the all-fp32 bound
 of the forward check path; every product and the carried state gradient are
 fp32 with fp32 accumulation, and the exponentials use the hardware exp2.
@@ -20,7 +21,7 @@ from workloads import WORKLOADS, make_inputs, random_inputs
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-4
-NAMES = ("dx", "ddt", "dA", "dB", "dC", "dD", "ddt_bias", "dinitial_states")
+NAMES = ("dx", "ddt", "dA", "dB", "dC", "dD", "dz", "ddt_bias", "dinitial_states")
 
 
 def _say(msg):
@@ -38,11 +39,11 @@ def rel_err(got, ref):
 def grads_both(ssd, d, dout, dfin, softplus=True, limit=(0.0, math.inf)):
     g = {k: (None if v is None else v.cuda()) for k, v in d.items()}
     got = ssd.ssd_bwd(g["x"], g["dt"], g["A"], g["B"], g["C"], dout.cuda(), 64, D=g["D"],
-                      dt_bias=g.get("dt_bias"), initial_states=g["initial_states"],
+                      z=g.get("z"), dt_bias=g.get("dt_bias"), initial_states=g["initial_states"],
                       dfinal_state=None if dfin is None else dfin.cuda(), dt_softplus=softplus,
                       dt_limit=limit)
     torch.cuda.synchronize()
-    ref = ssd_grads(d["x"], d["dt"], d["A"], d["B"], d["C"], dout, D=d["D"],
+    ref = ssd_grads(d["x"], d["dt"], d["A"], d["B"], d["C"], dout, D=d["D"], z=d.get("z"),
                     dt_bias=d.get("dt_bias"), initial_states=d["initial_states"],
                     dfinal_state=dfin, dt_softplus=softplus, dt_limit=limit)
     return got, ref
@@ -74,8 +75,8 @@ SHAPES = [(1, 64, 1, 1), (2, 100, 2, 1), (1, 257, 4, 2), (2, 130, 4, 4), (1, 33,
 def test_backward_matches_oracle(gpu_lib, shape, opts):
     Bsz, L, H, G = shape
     _say(f"  bwd B={Bsz} L={L} H={H} G={G} options={opts}")
-    d = random_inputs(Bsz, L, H, 64, 64, G, seed=Bsz * 100 + L + H, has_D=opts, has_h0=opts,
-                      dt_bias=opts)
+    d = random_inputs(Bsz, L, H, 64, 64, G, seed=Bsz * 100 + L + H, has_D=opts, has_z=opts,
+                      has_h0=opts, dt_bias=opts)
     dout, dfin = _dout((Bsz, L, H, 64), (Bsz, H, 64, 64), seed=L, fin=opts)
     got, ref = grads_both(gpu_lib, d, dout, dfin)
     compare(got, ref)
