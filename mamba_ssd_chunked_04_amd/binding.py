@@ -300,7 +300,9 @@ def causal_conv1d(x, weight, bias=None, conv_state=None, activation: str = "silu
     if weight.dim() != 2 or weight.shape[0] != D:
         raise ValueError("weight must be [D, W]")
     W = weight.shape[1]
-    act = {"silu": 1, None: 0, "none": 0}[activation]
+    if activation not in ("silu", "none", None):
+        raise ValueError(f"activation must be 'silu' or None, got {activation!r}")
+    act = 1 if activation == "silu" else 0
     if out is None:
         out = torch.empty_like(x)
     if return_final_state and final_state is None:
