@@ -781,6 +781,11 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   constexpr int KB = N / 32;  // K blocks over the state dim
   constexpr int NN = SS::NN;
   constexpr int LDN = N + 8, LDJ = kJB + 8, LDZ = kP + 4;
+  // hoist the fp16 M.X operand fragments out of the row-tile loop only when
+  // the state and output accumulators take fewer than 64 registers (with 64,
+  // as for 128-token chunks of a 128-wide state, the hoisted fragments spill;
+  // the fp32 check path keeps them unhoisted too)
+  constexpr bool kHoistX = !F32 && 4 * NN + 4 * NR * PT < 64;
   __shared__ __attribute__((aligned(16))) E sB[kJB * LDN];
   __shared__ __attribute__((aligned(16))) E sBT[N * LDJ];
   __shared__ __attribute__((aligned(16))) E sXT[kP * LDJ];
@@ -793,7 +798,9 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   const RowSpan rs = row_span(p, b);
   const int64_t ng_row = row_groups(p, rs.len), nc_row = row_chunks(p, rs.len);
   if (j >= ng_row) return;  // past the end of a shorter packed sequence
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lq = lane >> 4;
+  // the wave index is uniform: read it into a scalar so per-wave tests branch
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
   const int pt0 = RS::pt0(w);
   const int64_t g = h / (p.H / p.G);
   const SeqView<N, IO> sv(p, rs, h, g);
@@ -963,6 +970,27 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
           a0[kb] = *reinterpret_cast<const frag *>(&sB[(32 * js + lr) * LDN + 32 * kb + 8 * lq]);
           a1[kb] = *reinterpret_cast<const frag *>(&sB[(32 * js + 16 + lr) * LDN + 32 * kb + 8 * lq]);
         }
+        // x^T fragments of the sub-block (B operand of M.X; K slots j =
+        // 32 js + 4 lq + s and + 16).  When the accumulators leave room they
+        // are read once for all of the wave's row tiles, ahead of the B.C^T
+        // products; otherwise each row tile reads them as it needs them.
+        auto x_frag = [&](int pt) {
+          const E *xrow = &sXT[(16 * (pt0 + pt) + lr) * LDJ + 32 * js + 4 * lq];
+          const quad lo = *reinterpret_cast<const quad *>(xrow);
+          const quad hi = *reinterpret_cast<const quad *>(xrow + 16);
+          frag f;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            f[s] = lo[s];
+            f[4 + s] = hi[s];
+          }
+          return f;
+        };
+        frag xb[kHoistX ? PT : 1];
+        if constexpr (kHoistX) {
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) xb[pt] = x_frag(pt);
+        }
         const int ja0 = jbase + 4 * lq;
         const float lmid = cl.mid[jbase >> 5];
 #pragma unroll
@@ -1019,16 +1047,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
           }
 #pragma unroll
           for (int pt = 0; pt < PT; ++pt) {
-            const E *xrow = &sXT[(16 * (pt0 + pt) + lr) * LDJ + 32 * js + 4 * lq];
-            const quad lo = *reinterpret_cast<const quad *>(xrow);
-            const quad hi = *reinterpret_cast<const quad *>(xrow + 16);
-            frag xb;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              xb[s] = lo[s];
-              xb[4 + s] = hi[s];
-            }
-            yacc[k][pt] = mma(mf, xb, yacc[k][pt]);
+            if constexpr (kHoistX) yacc[k][pt] = mma(mf, xb[pt], yacc[k][pt]);
+            else yacc[k][pt] = mma(mf, x_frag(pt), yacc[k][pt]);
           }
         }
       }
