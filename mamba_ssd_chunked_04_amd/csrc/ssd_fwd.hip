@@ -823,13 +823,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   auto load_zb = [&](uint32_t tb) {
     if (HAS_Z) load_z<T>(rz, z_bf16, sv.H, sv.h, tb, nz);
   };
-  load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), nxt);
-  load_zb((uint32_t)(c_begin * Q));
   const rsrc_t rdt = make_rsrc(p.dt + rs.start * p.H, (uint32_t)(rs.len * p.H * 4));
   const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
-  // dt two chunks ahead in registers, one chunk ahead in LDS
-  stage_dt<Q>(load_dt(rdt, sv.H, sv.h, (uint32_t)(c_begin * Q), Q), clb[c_begin & 1]);
-  float dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c_begin + 1 < c_end ? c_begin + 1 : c_begin) * Q), Q);
   typename IO::raw8 craw[NR][KB];
   auto load_c = [&](uint32_t t0) {
 #pragma unroll
@@ -841,39 +836,60 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   // C rows are prefetched during the previous chunk's last block when they
   // fit in 16 registers, else loaded at the start of their chunk
   constexpr bool kPrefetchC = NR * KB * sizeof(typename IO::raw8) <= 64;
-  if (kPrefetchC) load_c((uint32_t)(c_begin * Q));
+
+  // Prologue.  Loads retire in issue order: the first two chunks' dt are
+  // asked for first, so staging dt does not wait for the first block; the
+  // block (its z, the first chunk's prefetched C rows) follows, then the
+  // initial state and the first R group aggregates, which arrive with the
+  // block instead of one round trip after it.
+  // dt two chunks ahead in registers, one chunk ahead in LDS.
+  const float dt0 = load_dt(rdt, sv.H, sv.h, (uint32_t)(c_begin * Q), Q);
+  float dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c_begin + 1 < c_end ? c_begin + 1 : c_begin) * Q), Q);
 
   // state entering this group: state_passing over the groups before it,
   // S = exp(Lam_grp[i]) S + S_grp[i] for i < j starting from h0 (or zero),
   // elementwise in this thread's share of the state; the aggregates are
-  // loaded R at a time (a missing h0 reads as zeros through an empty range).
-  // When the passing pass already chained the groups, slot j-1 holds the
-  // entering state: the same loop then runs once, from zero.
+  // loaded R at a time through a range holding slots i_begin..j-1 (a missing
+  // h0, and slots past j-1, read as zeros through the range check).  When the
+  // passing pass already chained the groups, slot j-1 holds the entering
+  // state: the same loop then runs once, from zero.
   f32x4 sacc[NN];
   {
     const bool from_zero = p.chained && j > 0;
     const int64_t i_begin = from_zero ? j - 1 : 0;
     const float *h0 = (p.h0 && !from_zero) ? p.h0 + bh * (int64_t)(kP * N) : nullptr;
     const rsrc_t ri = make_rsrc(h0, h0 ? (uint32_t)(kP * N * 4) : 0u);
+    constexpr int R = 16 / NN > 0 ? 16 / NN : 1;
+    const int64_t ng1 = p.ngroups - 1;
+    // at most kFoldGroups + 1 slots (one when chained): far below 2^32 bytes
+    const rsrc_t ra = make_rsrc(j > i_begin ? p.grp_state + (bh * ng1 + i_begin) * (int64_t)(kP * N)
+                                            : nullptr,
+                                (uint32_t)((j - i_begin) * (kP * N * 4)));
+    const float *glam = p.grp_lam + bh * ng1;
+    load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), nxt);
+    load_zb((uint32_t)(c_begin * Q));
+    if (kPrefetchC) load_c((uint32_t)(c_begin * Q));
+    f32x4 v[R][NN];
+    auto load_aggs = [&](int64_t i0) {
+#pragma unroll
+      for (int q = 0; q < R; ++q)
+#pragma unroll
+        for (int t = 0; t < NN; ++t)
+          v[q][t] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         ra, (uint32_t)(((i0 - i_begin + q) * (kP * N) + (t * T + threadIdx.x) * 4) * 4),
+                         0, 0));
+    };
 #pragma unroll
     for (int t = 0; t < NN; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         sacc[t][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
             ri, (uint32_t)(SS::row(r) * N + SS::col(t)) * 4, 0, 0));
-    constexpr int R = 16 / NN > 0 ? 16 / NN : 1;
-    const int64_t ng1 = p.ngroups - 1;
-    const float *agg = p.grp_state + bh * ng1 * (int64_t)(kP * N);
-    const float *glam = p.grp_lam + bh * ng1;
+    load_aggs(i_begin);
+    stage_dt<Q>(dt0, clb[c_begin & 1]);
     for (int64_t i0 = i_begin; i0 < j; i0 += R) {
-      f32x4 v[R][NN];
-#pragma unroll
-      for (int q = 0; q < R; ++q) {
-        const int64_t i = (i0 + q < j) ? i0 + q : j - 1;
-#pragma unroll
-        for (int t = 0; t < NN; ++t)
-          v[q][t] = *reinterpret_cast<const f32x4 *>(agg + i * (kP * N) + (t * T + threadIdx.x) * 4);
-      }
+      if (i0 != i_begin) load_aggs(i0);
 #pragma unroll
       for (int q = 0; q < R; ++q) {
         if (i0 + q >= j) break;
