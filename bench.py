@@ -539,8 +539,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
-              f"multi-GPU path; see DESIGN.md for how the SSD forward would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): there is no "
+              f"multi-GPU path; the forward would shard over (b, h) with no exchange, or "
+              f"over L with one exchange of per-span states.", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

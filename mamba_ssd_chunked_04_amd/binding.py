@@ -55,8 +55,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         return _lib
     p = path or os.environ.get("SSD_MI355X_LIB", LIB)
     if not os.path.exists(p):
-        raise RuntimeError(f"HIP library {p} is missing: run __graft_entry__.build() "
-                           f"(or python -m mamba_ssd_chunked_04_amd.build) first")
+        raise RuntimeError(f"HIP library {p} is missing: build it first with "
+                           f"python -m mamba_ssd_chunked_04_amd.build")
     lib = ctypes.CDLL(p)
     vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     dp = ctypes.POINTER(SsdDesc)

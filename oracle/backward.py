@@ -15,7 +15,7 @@ chunking.  With z the output is gated as in the forward, out = y * silu(z),
 and dz is returned.  Pinned by central finite differences of the fp64 C
 recurrence in tests/test_oracle_backward.py.
 
-Readings (listed again in the design doc): the gradient of the clamp is zero
+Readings: the gradient of the clamp is zero
 where dt is clamped (the inputs keep away from the edges); dA sums over all
 batch rows and tokens; dD and ddt_bias likewise.
 """

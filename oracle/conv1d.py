@@ -8,7 +8,7 @@ convolution of width 4 over the time axis, then SiLU, feeding the SSM) and
 and a per-channel bias; its test builds the reference as a grouped conv1d
 with groups = D, stride 1, padding W-1, cut to the first S steps, then SiLU).
 
-Readings where the page is silent or garbled (listed again in the design doc):
+Readings where the page is silent or garbled:
   * w is [D, W] (the table's "w BDS" is an extraction garble; a depthwise
     kernel holds W taps per channel); tap k multiplies x[t - (W-1) + k], the
     cross-correlation of a conv1d padded by W-1 on the left, so w[:, W-1]

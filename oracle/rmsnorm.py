@@ -7,7 +7,7 @@ the input x is gated by SiLU(z), normalised by an RMSNorm taken over groups
 of the last dimension, and multiplied by a weight w.  x, z and out are
 [B, S, D] fp32, w is [D]; the parameters are the group count G and eps.
 
-Readings where the page is silent (listed again in the design doc):
+Readings where the page is silent:
   * the G groups are contiguous blocks of D/G elements of the last dimension;
   * the RMS of a group is sqrt(mean(g^2) + eps), eps inside the root;
   * SiLU(v) = v * sigmoid(v);

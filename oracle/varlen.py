@@ -6,7 +6,7 @@ along the token axis, delimited by cumulative start offsets).
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Readings where the pages are silent (listed again in the design doc):
+Readings where the pages are silent:
   * the tokens of nseq sequences are concatenated along one token axis of
     length T; cu_seqlens [nseq+1] holds the start offset of each sequence
     and T last (cu_seqlens[0] = 0, non-decreasing); a sequence may be empty;
