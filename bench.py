@@ -48,6 +48,15 @@ PAGE_TOKENS_PER_S = {"same_device": 4 * 2048 / 0.632e-3,
                      "h256": 8 * 4096 / 31.888e-3}
 
 
+def quantile(v, q: float) -> float:
+    """Linear-interpolated quantile of a non-empty list."""
+    v = sorted(v)
+    x = q * (len(v) - 1)
+    i = int(math.floor(x))
+    j = min(i + 1, len(v) - 1)
+    return v[i] + (v[j] - v[i]) * (x - i)
+
+
 def algorithmic_bytes(w: Workload, ret_final: bool = True) -> int:
     """Bytes the forward must move at least once: every input read once,
     every output written once."""
@@ -632,6 +641,7 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "kernel": "ssd_chunk_scan_kernel", "kernel_ms": main_mean,
+                     "kernel_ms_p20_p50_p80": [quantile(main_ms, q) for q in (0.2, 0.5, 0.8)],
                      "algorithmic_bytes": abytes},
         "path": {"ms": ms_per_step, "gbs": abytes / (wall / K) / 1e9,
                  "hbm_frac": abytes / (wall / K) / 1e9 / HBM_PEAK_GBS,
