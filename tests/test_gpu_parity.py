@@ -229,6 +229,36 @@ def test_graph_capture_replays_match_eager(gpu_lib, cpw):
         del junk
 
 
+def test_largest_row_under_the_32bit_offset_limit(gpu_lib):
+    """One batch row whose x and out slices are one token short of 2 GiB, the
+    largest the 32-bit buffer offsets address (131071 tokens of 64 heads,
+    a ragged last chunk, eight chunk groups): sampled heads, first and last,
+    against the oracle, output and final state."""
+    H, P, N, G, Q = 64, 64, 128, 1, 128
+    L = (2 ** 31 - 1) // (H * P * 4)
+    _say(f"[case] largest row [1,{L},{H},{P},{N},{Q},{G}] (x bytes {L * H * P * 4})")
+    assert L * H * P * 4 < 2 ** 31 <= (L + 1) * H * P * 4
+    g = torch.Generator(device="cuda").manual_seed(20260 + 99)
+    x = torch.randn(1, L, H, P, device="cuda", generator=g)
+    dt = torch.rand(1, L, H, device="cuda", generator=g)
+    A = -torch.rand(H, device="cuda", generator=g)
+    Bm = torch.randn(1, L, G, N, device="cuda", generator=g)
+    Cm = torch.randn(1, L, G, N, device="cuda", generator=g)
+    out, fin = gpu_lib.ssd_fwd(x, dt, A, Bm, Cm, Q, dt_softplus=True, return_final_state=True)
+    torch.cuda.synchronize()
+    Bc, Cc = Bm.cpu(), Cm.cpu()
+    for h in (0, H - 1):
+        ref_out, ref_fin = oracle_run({"x": x[:, :, h:h + 1].cpu(), "dt": dt[:, :, h:h + 1].cpu(),
+                                       "A": A[h:h + 1].cpu(), "B": Bc, "C": Cc})
+        assert_close(out[:, :, h:h + 1].cpu().numpy(), ref_out, TOL["f16"], f"out (h={h})")
+        assert_close(fin[:, h:h + 1].cpu().numpy(), ref_fin, TOL["f16"], f"final (h={h})")
+        # the last tokens, whose byte offsets are the largest of the row
+        assert_close(out[:, -200:, h:h + 1].cpu().numpy(), ref_out[:, -200:], TOL["f16"],
+                     f"last 200 rows (h={h})")
+    del x, dt, A, Bm, Cm, out, fin
+    torch.cuda.empty_cache()
+
+
 def test_invalid_calls_raise(gpu_lib):
     d = to_gpu(random_inputs(1, 64, 2, 64, 64, 1, seed=404))
     with pytest.raises(NotImplementedError):
