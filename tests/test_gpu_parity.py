@@ -75,6 +75,10 @@ SMALL = [
     ("q64_n128_bf16", 1, 257, 4, 128, 4, 64, True, True, True, False, "bf16", None),
     ("q128_n64_limit", 2, 390, 2, 64, 1, 128, False, False, False, True, "f32", (0.8, 1.1)),
     ("q256_n64_bf16_gate", 1, 513, 4, 64, 2, 256, True, True, False, False, "bf16", None),
+    # eight or more heads per B/C group: C.B^T formed once per group
+    ("q64_g1_h8_tail_D_h0", 1, 300, 8, 64, 1, 64, True, False, True, False, "f32", None),
+    ("q128_g1_h8_bf16_gate", 2, 400, 8, 128, 1, 128, True, True, True, True, "bf16", None),
+    ("q256_g2_h16_tail", 1, 700, 16, 128, 2, 256, False, False, False, False, "f32", None),
 ]
 
 
