@@ -79,6 +79,8 @@ SMALL = [
     ("q64_g1_h8_tail_D_h0", 1, 300, 8, 64, 1, 64, True, False, True, False, "f32", None),
     ("q128_g1_h8_bf16_gate", 2, 400, 8, 128, 1, 128, True, True, True, True, "bf16", None),
     ("q256_g2_h16_tail", 1, 700, 16, 128, 2, 256, False, False, False, False, "f32", None),
+    ("q128_h4_g2_D_h0_bias", 2, 700, 4, 128, 2, 128, True, False, True, True, "f32", None),
+    ("q128_n64_bf16_limit", 1, 333, 8, 64, 2, 128, True, False, True, False, "bf16", (0.8, 1.2)),
 ]
 
 
