@@ -173,6 +173,8 @@ struct Params {
                      // start), or entering states once the passing pass ran
   float *grp_lam;    // [B*H][ngroups-1]: group total log2-decay
   const int32_t *cu_seqlens;  // packed calls: [batch+1] token offsets, else NULL
+  int32_t *error_flag;        // packed calls: set to 1 on offsets that break the contract
+  int64_t packed_tokens;      // packed calls: T when known (offsets are clamped to it), else 0
   int64_t batch, L, H, G, nc, ngroups, cpg;
   int Q;
   float dt_min, dt_max;
@@ -215,18 +217,33 @@ __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_her
 }
 
 // Tokens of batch row b: [start, start + len) on the token axis.  Dense
-// calls: b*L and L.  Packed calls: the row is sequence b of cu_seqlens, its
-// length clamped to [0, L] (L is then the longest sequence, which the plan
-// is made for).
+// calls: b*L and L.  Packed calls: the row is sequence b of cu_seqlens,
+// with its offsets clamped to [0, T] (when T is known) and its length to
+// [0, L] (L is then the longest sequence, which the plan is made for), so
+// that malformed offsets never address memory outside x, B, C and out; the
+// main pass reports them through error_flag (offsets_break_contract).
 struct RowSpan {
   int64_t start, len;
 };
 
 __device__ __forceinline__ RowSpan row_span(const Params &p, int64_t b) {
   if (!p.cu_seqlens) return {b * p.L, p.L};
-  const int64_t s = p.cu_seqlens[b], e = p.cu_seqlens[b + 1];
+  int64_t s = p.cu_seqlens[b], e = p.cu_seqlens[b + 1];
+  s = s < 0 ? 0 : s;
+  if (p.packed_tokens > 0) {
+    s = s > p.packed_tokens ? p.packed_tokens : s;
+    e = e > p.packed_tokens ? p.packed_tokens : e;
+  }
   const int64_t len = e - s;
   return {s, len < 0 ? 0 : (len > p.L ? p.L : len)};
+}
+
+// Whether the offsets of packed row b break the contract of the call: a
+// sequence longer than L, decreasing offsets, a negative offset or one past
+// T (when T is known).
+__device__ __forceinline__ bool offsets_break_contract(const Params &p, int64_t b) {
+  const int64_t s = p.cu_seqlens[b], e = p.cu_seqlens[b + 1];
+  return s < 0 || e < s || e - s > p.L || (p.packed_tokens > 0 && e > p.packed_tokens);
 }
 
 // Chunks of a row and the chunk groups that hold them; an empty row keeps
@@ -341,7 +358,10 @@ __device__ __forceinline__ void chunk_prep(const Params &p, uint32_t t0, uint64_
 #pragma unroll
   for (int m = 0; m < Q / 64; ++m) {
     float u = cl.dts[lane + 64 * m] + bias;
-    if (p.dt_softplus) u = (u > 20.f) ? u : __logf(1.f + __expf(u));
+    // softplus as max(u, 0) + log1p(exp(-|u|)): no cancellation for negative
+    // u (where log(1 + exp(u)) loses the digits of a small step) and no
+    // overflow for large u; the backward uses the same form
+    if (p.dt_softplus) u = fmaxf(u, 0.f) + log1pf(__expf(-fabsf(u)));
     const float delta = (t0 + lane + 64 * m < len) ? fminf(fmaxf(u, p.dt_min), p.dt_max) : 0.f;
     const float a = delta * a_h * kLog2e;
     big |= fabsf(a) > 7.f;
@@ -795,6 +815,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
 
   int64_t b, h, j;
   if (!decode_tile(p, p.ngroups, b, h, j, true)) return;
+  if (p.cu_seqlens && p.error_flag && j == 0 && threadIdx.x == 0 && offsets_break_contract(p, b))
+    __builtin_amdgcn_raw_buffer_store_b32(1u, make_rsrc(p.error_flag, 4u), 0, 0, 0);
   const RowSpan rs = row_span(p, b);
   const int64_t ng_row = row_groups(p, rs.len), nc_row = row_chunks(p, rs.len);
   if (j >= ng_row) return;  // past the end of a shorter packed sequence
@@ -1337,7 +1359,7 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B
       (d->z && !aligned16(d->z)) || !aligned16(dt) ||
       (d->initial_state && !aligned16(d->initial_state)) ||
       (return_final_state && !aligned16(final_state)) ||
-      ((uintptr_t)d->cu_seqlens & 3u) != 0)
+      ((uintptr_t)d->cu_seqlens & 3u) != 0 || ((uintptr_t)d->error_flag & 3u) != 0)
     return SSD_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, chunk);
   const size_t need = pl.total();
@@ -1361,6 +1383,8 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B
   prm.grp_state = pl.state_bytes ? reinterpret_cast<float *>(ws) : nullptr;
   prm.grp_lam = pl.lam_bytes ? reinterpret_cast<float *>(ws + pl.state_bytes) : nullptr;
   prm.cu_seqlens = d->cu_seqlens;
+  prm.error_flag = d->cu_seqlens ? d->error_flag : nullptr;
+  prm.packed_tokens = d->cu_seqlens ? d->packed_tokens : 0;
   prm.batch = d->batch;
   prm.L = d->seqlen;
   prm.Q = (int)chunk;

@@ -141,21 +141,47 @@ def packed_inputs(seqlens: Sequence[int], H: int, P: int, N: int, G: int, seed: 
 
 def random_inputs(Bsz: int, L: int, H: int, P: int, N: int, G: int, seed: int,
                   has_D: bool = False, has_z: bool = False, has_h0: bool = False,
-                  io_dtype: str = "f32", dt_bias: bool = False) -> Dict[str, Optional[torch.Tensor]]:
+                  io_dtype: str = "f32", dt_bias: bool = False,
+                  bias_range: Optional[Tuple[float, float]] = None,
+                  A_range: Optional[Tuple[float, float]] = None,
+                  A_value: Optional[float] = None,
+                  scale: Optional[float] = None) -> Dict[str, Optional[torch.Tensor]]:
     """Inputs of an arbitrary small shape, same distributions as the workloads.
 
     With ``dt_bias`` an extra per-head bias ~ U(-1, 0) is drawn after the
-    other tensors.
+    other tensors; ``bias_range = (lo, hi)`` draws it ~ U(lo, hi) instead
+    (the same generator).  ``A_range = (lo, hi)`` redraws A = -U(lo, hi) per
+    head from a generator of its own; ``A_value`` sets every A[h] to that
+    value.  ``scale`` multiplies x, B and C by it (before any cast), for
+    magnitudes outside the standard normal's range.  Drawn after everything
+    else, these leave the other tensors' bits unchanged.
     """
     w = Workload("adhoc", Bsz, L, H, P, N, 64, G, has_D=has_D, has_z=has_z,
                  has_h0=has_h0, io_dtype=io_dtype, seed=seed)
-    d = make_inputs(w)
-    if dt_bias:
+    if scale is not None:
+        d = make_inputs(w.scaled(io_dtype="f32"))
+        io = _TORCH_DTYPES[io_dtype]
+        for k in ("x", "B", "C"):
+            d[k] = (d[k] * scale).to(io)
+    else:
+        d = make_inputs(w)
+    if dt_bias or bias_range is not None:
         g = torch.Generator(device="cpu")
         g.manual_seed(seed + 7919)
-        d["dt_bias"] = -torch.rand(H, generator=g, dtype=torch.float32)
+        if bias_range is None:
+            d["dt_bias"] = -torch.rand(H, generator=g, dtype=torch.float32)
+        else:
+            lo, hi = bias_range
+            d["dt_bias"] = lo + (hi - lo) * torch.rand(H, generator=g, dtype=torch.float32)
     else:
         d["dt_bias"] = None
+    if A_range is not None:
+        g = torch.Generator(device="cpu")
+        g.manual_seed(seed + 104729)
+        lo, hi = A_range
+        d["A"] = -(lo + (hi - lo) * torch.rand(H, generator=g, dtype=torch.float32))
+    if A_value is not None:
+        d["A"] = torch.full((H,), float(A_value), dtype=torch.float32)
     return d
 
 
