@@ -107,9 +107,12 @@ typedef struct ssd_desc {
                                 after its last token; initial_state and
                                 final_state stay [batch,H,P,N].  `seqlen`
                                 is then the longest sequence: the plan is
-                                made for it, and a longer sequence is
-                                processed only up to `seqlen` tokens (the
-                                out rows past that are not written).
+                                made for it.  A call whose offsets break
+                                that contract (a sequence longer than
+                                `seqlen`, decreasing offsets, or an offset
+                                past packed_tokens when that is given)
+                                leaves those sequences' results undefined
+                                and sets *error_flag (below).
                                 Readings of page "Mamba-2 SSD for Ascend
                                 NPU", "Limitations and roadmap" (varlen,
                                 cu_seqlens) and page "ops-transformer
@@ -120,6 +123,15 @@ typedef struct ssd_desc {
                                 spread the work of uneven lengths; 0 plans
                                 as if every sequence had `seqlen` tokens.
                                 Ignored for dense calls                   */
+  int32_t *error_flag;       /* optional DEVICE int32, or NULL.  With
+                                cu_seqlens, the kernels store 1 into it
+                                when the offsets break the contract above
+                                (the offsets live on the device, so this is
+                                the only place such an error can surface
+                                without a synchronisation).  The library
+                                never clears it: the caller zeroes it and
+                                reads it after synchronising.  Ignored for
+                                dense calls                               */
 } ssd_desc;
 
 /* Fills `d` with defaults for the given shape: fp32 storage, fp16 MMA, no
@@ -240,7 +252,7 @@ const char *ssd_status_str(int status);
 /* ABI version of this header (bumped on any incompatible change). */
 int ssd_abi_version(void);
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -36,6 +36,7 @@ class SsdDesc(ctypes.Structure):
         ("chunks_per_wg", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p),
         ("cu_seqlens", ctypes.c_void_p), ("packed_tokens", ctypes.c_int64),
+        ("error_flag", ctypes.c_void_p),
     ]
 
 
@@ -137,16 +138,30 @@ class SsdCall:
     stream handle (an int from ``torch.cuda.Stream.cuda_stream``).
     """
 
-    def __init__(self, args, desc: SsdDesc, keep):
+    def __init__(self, args, desc: SsdDesc, keep, error_flag=None):
         self._args = args
         self.desc = desc
         self._keep = keep        # tensors whose storage the pointers refer to
+        self.error_flag = error_flag   # packed calls: the device flag the kernels set
 
     def launch(self, stream: int) -> None:
         a = self._args
         st = load_library().ssd_fwd(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9],
                                     a[10], ctypes.c_void_p(stream), ctypes.byref(self.desc))
         _raise_for(st, "ssd_fwd")
+
+    def check(self) -> None:
+        """Packed calls: synchronise and raise ValueError if any launch of this
+        call found cu_seqlens breaking its contract (a sequence longer than
+        max_seqlen, decreasing offsets or one past the packed tokens); the
+        flag is then cleared.  A no-op for dense calls."""
+        if self.error_flag is None:
+            return
+        if int(self.error_flag.item()) != 0:
+            self.error_flag.zero_()
+            raise ValueError("ssd_fwd: cu_seqlens breaks the call's contract (a sequence longer "
+                             "than max_seqlen, decreasing offsets or an offset past the packed "
+                             "tokens); the results of those sequences are undefined")
 
 
 def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initial_states=None,
@@ -163,7 +178,10 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     [1, T, G, N], z like x) with ``cu_seqlens`` an int32 GPU tensor of
     nseq+1 token offsets; initial and final states are then [nseq, H, P, N].
     ``max_seqlen`` (the longest sequence) is read from cu_seqlens when not
-    given, which synchronises with the device.
+    given, which synchronises with the device and checks the offsets (0
+    first, never decreasing, T last; ValueError otherwise).  When it is
+    given nothing is read: offsets that break the contract are reported by
+    the kernels through a device flag, which ``call.check()`` reads.
     Returns (call, out, final_state_or_None, workspace_or_None).
     """
     import torch
@@ -184,7 +202,15 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
                              "on the GPU of x")
         nrows = cu_seqlens.numel() - 1
         if max_seqlen is None:
-            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
+            # reading the offsets synchronises anyway: check them whole here
+            cu = cu_seqlens.cpu()
+            lens = cu[1:] - cu[:-1]
+            if int(cu[0]) != 0 or bool((lens < 0).any()) or int(cu[-1]) != L:
+                raise ValueError(f"cu_seqlens must start at 0, never decrease and end at the "
+                                 f"packed token count {L}")
+            max_seqlen = int(lens.max())
+        elif int(max_seqlen) < 1:
+            raise ValueError("max_seqlen must be >= 1")
         row_len = max(1, int(max_seqlen))
     if dt.shape != (Bsz, L, H) or A.shape != (H,) or B.shape != (Bsz, L, G, N) or C.shape != B.shape:
         raise ValueError("shape mismatch: x[B,L,H,P], dt[B,L,H], A[H], B/C[B,L,G,N]")
@@ -209,9 +235,12 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     if return_final_state and final_state is None:
         final_state = torch.empty(nrows, H, P, N, device=dev, dtype=torch.float32)
     desc = make_desc(nrows, row_len, H, P, N, G)
+    error_flag = None
     if cu_seqlens is not None:
         desc.cu_seqlens = cu_seqlens.data_ptr()
         desc.packed_tokens = L
+        error_flag = torch.zeros(1, device=dev, dtype=torch.int32)
+        desc.error_flag = error_flag.data_ptr()
     desc.x_dtype = _dtype_code(x.dtype)
     desc.z_dtype = _dtype_code(z.dtype) if z is not None else SSD_F32
     desc.out_dtype = _dtype_code(out.dtype)
@@ -227,19 +256,27 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk_size),
             int(bool(dt_softplus)), int(bool(return_final_state)), _ptr(out),
             _ptr(final_state) if return_final_state else None)
-    keep = (x, dt, A, B, C, D, z, dt_bias, initial_states, out, final_state, workspace, cu_seqlens)
-    return SsdCall(args, desc, keep), out, (final_state if return_final_state else None), workspace
+    keep = (x, dt, A, B, C, D, z, dt_bias, initial_states, out, final_state, workspace, cu_seqlens,
+            error_flag)
+    return (SsdCall(args, desc, keep, error_flag), out,
+            (final_state if return_final_state else None), workspace)
 
 
 def ssd_fwd(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initial_states=None,
             dt_softplus: bool = False, dt_limit: Tuple[float, float] = (0.0, math.inf),
             return_final_state: bool = False, mma: str = "f16", out_dtype=None,
-            chunks_per_wg: int = 0, cu_seqlens=None, max_seqlen: Optional[int] = None):
+            chunks_per_wg: int = 0, cu_seqlens=None, max_seqlen: Optional[int] = None,
+            check_offsets: bool = True):
     """SSD chunked forward on the current torch stream.
 
     Returns ``out`` or ``(out, final_state)`` when ``return_final_state``.
     With ``cu_seqlens`` the call runs packed variable-length sequences (see
-    ``prepare``).
+    ``prepare``); when ``max_seqlen`` is given, ``check_offsets`` (default
+    True) synchronises after the launch and raises ValueError if a sequence
+    was longer than it (or the offsets were malformed).  Pass
+    ``check_offsets=False`` to skip that synchronisation (then nothing
+    reports such offsets; ``prepare`` and ``call.check()`` give control over
+    when the check runs).
     """
     import torch
     call, out, fin, _ws = prepare(x, dt, A, B, C, chunk_size, D=D, z=z, dt_bias=dt_bias,
@@ -249,6 +286,8 @@ def ssd_fwd(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
                                   cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
     with torch.cuda.device(x.device):
         call.launch(torch.cuda.current_stream(x.device).cuda_stream)
+        if cu_seqlens is not None and max_seqlen is not None and check_offsets:
+            call.check()
     return (out, fin) if return_final_state else out
 
 

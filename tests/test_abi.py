@@ -44,11 +44,11 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(bnd.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), f"{name} not exported"
-    assert lib.ssd_abi_version() == 2
+    assert lib.ssd_abi_version() == 3
 
 
 def test_desc_layout_matches_c(lib):
-    assert ctypes.sizeof(bnd.SsdDesc) == 152
+    assert ctypes.sizeof(bnd.SsdDesc) == 160
     d = bnd.SsdDesc()
     ctypes.memset(ctypes.byref(d), 0x5A, ctypes.sizeof(d))
     lib.ssd_desc_init(ctypes.byref(d), 3, 5, 7, 64, 128, 7)
@@ -59,7 +59,7 @@ def test_desc_layout_matches_c(lib):
     assert d.z is None and d.dt_bias is None and d.initial_state is None and d.workspace is None
     assert d.workspace_bytes == 0 and d.chunks_per_wg == 0 and d.reserved == 0
     assert d.ev_main_begin is None and d.ev_main_end is None and d.cu_seqlens is None
-    assert d.packed_tokens == 0
+    assert d.packed_tokens == 0 and d.error_flag is None
 
 
 def test_status_strings(lib):

@@ -107,23 +107,50 @@ def test_packed_equals_dense_rows(gpu_lib):
     assert torch.equal(o_p.reshape(o_d.shape), o_d) and torch.equal(f_p, f_d)
 
 
-def test_sequence_longer_than_max_seqlen_is_clamped(gpu_lib):
-    # the documented contract: a sequence longer than max_seqlen is processed
-    # up to max_seqlen tokens; its remaining out rows are left as they were
+def test_sequence_longer_than_max_seqlen_is_reported(gpu_lib):
+    """A sequence longer than the max_seqlen the caller gave: the kernels set
+    the call's device error flag and check() raises; the sequences that keep
+    the contract are still right."""
     d = packed_inputs((50, 90), 4, 64, 64, 1, seed=94)
     g = {k: (None if v is None else v.cuda()) for k, v in d.items()}
-    out = torch.full((1, 140, 4, 64), 7.0, device="cuda")
     call, out, fin, _ = gpu_lib.prepare(g["x"], g["dt"], g["A"], g["B"], g["C"], 64,
                                         dt_softplus=True, return_final_state=True,
-                                        cu_seqlens=g["cu_seqlens"], max_seqlen=60, out=out)
+                                        cu_seqlens=g["cu_seqlens"], max_seqlen=60)
     call.launch(torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    cu = [0, 50, 110]
-    ro, rf = ssd_varlen(d["x"][:, :110], d["dt"][:, :110], d["A"], d["B"][:, :110], d["C"][:, :110], cu,
-                        dt_softplus=True)
-    o = out[0].cpu().numpy()
-    assert rel_err(o[:110], ro) <= TOL["f16"] and rel_err(fin.cpu().numpy(), rf) <= TOL["f16"]
-    assert (o[110:] == 7.0).all()
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        call.check()
+    call.check()                  # the flag was cleared with the report
+    ro, rf = ssd_varlen(d["x"][:, :50], d["dt"][:, :50], d["A"], d["B"][:, :50], d["C"][:, :50],
+                        [0, 50], dt_softplus=True)
+    assert rel_err(out[0, :50].cpu().numpy(), ro) <= TOL["f16"]
+    assert rel_err(fin[:1].cpu().numpy(), rf) <= TOL["f16"]
+    # the convenience call checks by default when max_seqlen is given
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        gpu_lib.ssd_fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], 64, dt_softplus=True,
+                        cu_seqlens=g["cu_seqlens"], max_seqlen=60)
+    # and a max_seqlen that holds raises nothing
+    gpu_lib.ssd_fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], 64, dt_softplus=True,
+                    cu_seqlens=g["cu_seqlens"], max_seqlen=90)
+
+
+def test_malformed_offsets_are_clamped_and_reported(gpu_lib):
+    """Offsets past the packed token count or decreasing: the kernels clamp
+    every sequence to [0, T] (nothing outside x, B, C or out is addressed)
+    and report the call; host-read offsets are refused before any launch."""
+    d = packed_inputs((40, 30, 30), 4, 64, 64, 1, seed=95)
+    g = {k: (None if v is None else v.cuda()) for k, v in d.items()}
+    for bad in ([0, 40, 30, 100], [0, 40, 70, 130]):
+        cu = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        call, out, fin, _ = gpu_lib.prepare(g["x"], g["dt"], g["A"], g["B"], g["C"], 64,
+                                            dt_softplus=True, return_final_state=True,
+                                            cu_seqlens=cu, max_seqlen=64)
+        call.launch(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        with pytest.raises(ValueError, match="cu_seqlens"):
+            call.check()
+        with pytest.raises(ValueError, match="cu_seqlens"):
+            gpu_lib.prepare(g["x"], g["dt"], g["A"], g["B"], g["C"], 64, cu_seqlens=cu)
 
 
 def test_varlen_workload_full_size(gpu_lib):
