@@ -7,12 +7,14 @@ step reads its inputs from HBM rather than from a cache warmed by the
 previous step.
 
 Prints ONE JSON line: whole-step throughput (tokens/s), plus
-  roofline     -- the main-pass kernel (ssd_chunk_scan_kernel), timed live
-                  with HIP events recorded around its launch on every 8th
-                  timed step (--event-every; an event pair on every step
-                  would itself lengthen the steps); achieved = algorithmic
-                  bytes / its mean duration;
-  cpu_baseline -- the fp64 oracle on this host's cores over a bounded sample.
+  roofline     -- the whole ssd_fwd call (every kernel it launches), timed
+                  live by a HIP event pair on the launch stream around the K
+                  back-to-back timed calls; achieved = algorithmic bytes /
+                  the mean GPU time of one call.  A sampling phase after the
+                  timed region splits a call over its kernels (``split``);
+  cpu_baseline -- the oracle's recurrence on this host's cores over a bounded
+                  sample (the fp32 instance; the fp64 oracle and one-thread
+                  runs alongside).
 
 ``--op rmsnorm_gated`` instead times the gated grouped RMSNorm that follows
 the SSD forward (page "ops-transformer MambaV2 算子套件", section 4.6) on the
@@ -101,8 +103,25 @@ def measured_traffic(name: str, kernel: str = "ssd_chunk_scan_kernel",
     with open(src, "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != rec.get("kernel_source_sha256"):
             return None
-    k = rec.get("workloads", {}).get(name, {}).get(kernel)
+    wl = rec.get("workloads", {}).get(name, {})
+    if kernel == "ssd_fwd":
+        # every kernel of one call; None unless the record lists the whole call
+        if not wl.get("whole_call"):
+            return None
+        ks = [v for v in wl.values() if isinstance(v, dict) and "fetch_bytes" in v]
+        return int(sum(k["fetch_bytes"] + k["write_bytes"] for k in ks)) if ks else None
+    k = wl.get(kernel)
     return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def kernel_list(ngroups: int) -> str:
+    """The kernels one ssd_fwd call launches for a plan with `ngroups` chunk
+    groups per (b, h) (the group passes only when a sequence is cut)."""
+    if ngroups <= 1:
+        return "ssd_chunk_scan_kernel"
+    if ngroups - 1 > 8:
+        return "ssd_group_state_kernel, ssd_group_passing_kernel, ssd_chunk_scan_kernel"
+    return "ssd_group_state_kernel, ssd_chunk_scan_kernel"
 
 
 class HipEvents:
@@ -161,46 +180,80 @@ def gpu_input_set(w: Workload, seed: int, device: str):
     return d
 
 
-def cpu_baseline(w: Workload, budget_s: float):
-    """The fp64 oracle, as it stands, on this host's cores, over a bounded
-    sample of the same workload: whole (b, h) sequences, repeated until about
-    ``budget_s`` seconds of CPU work, scaled to tokens/s of the workload."""
-    from oracle import oracle_max_threads, ssd_recurrence
-    d = make_inputs(w)
-    if w.packed:
-        return packed_cpu_baseline(w, d, budget_s, oracle_max_threads())
-    BH = w.batch * w.nheads
-    all_pairs = [(b, h) for b in range(w.batch) for h in range(w.nheads)]
-    threads = oracle_max_threads()
+def host_cpu() -> dict:
+    """The host's CPU model and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
 
-    def run(pairs):
-        t0 = time.perf_counter()
-        ssd_recurrence(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
-                       initial_states=d["initial_states"], dt_softplus=True, pairs=pairs)
-        return time.perf_counter() - t0
 
-    # probe: one sequence per thread (spread over the workload)
-    n = min(BH, threads)
-    stride = max(1, BH // n)
-    t_probe = run(all_pairs[::stride][:n])
-    per_round = t_probe                      # one round = `threads` sequences in parallel
-    rounds_full = math.ceil(BH / n)
-    t_full_est = per_round * rounds_full
-    if t_full_est <= budget_s:
-        pairs = all_pairs
-    else:
-        n_pairs = max(n, min(BH, int(budget_s / per_round) * n))
-        pairs = all_pairs[::max(1, BH // n_pairs)][:n_pairs]
-    # repeat the sample until the budget is spent (at least once)
+def _time_pairs(fn, d, pairs, threads: int, budget_s: float):
+    """Seconds per run of the recurrence over `pairs`, repeated until about
+    `budget_s` (at least once); returns (seconds per run, repetitions)."""
     t, reps = 0.0, 0
     while reps == 0 or t + t / reps <= budget_s:
-        t += run(pairs)
+        t0 = time.perf_counter()
+        fn(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+           initial_states=d["initial_states"], dt_softplus=True, pairs=pairs, nthreads=threads)
+        t += time.perf_counter() - t0
         reps += 1
-    t_full = t / reps * BH / len(pairs)
-    return {"value": w.tokens / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(pairs)} of {BH} (b,h) sequences of the {w.shape_str()} workload, "
-                      f"{reps} repetition(s), {t:.1f} s of fp64 recurrence on {threads} OpenMP "
-                      f"threads; scaled to the whole workload"}
+    return t / reps, reps
+
+
+def cpu_baseline(w: Workload, budget_s: float):
+    """The oracle's token recurrence, as it stands, on this host's cores over a
+    bounded sample of the same workload (whole (b, h) sequences), scaled to
+    tokens/s of the whole workload.  ``value`` is its float instance (the
+    precision of the public tensors); the fp64 oracle itself and one-thread
+    runs (this workload's sample and the tiny workload) are reported
+    alongside."""
+    from oracle import oracle_max_threads, ssd_recurrence, ssd_recurrence_f32
+    d = make_inputs(w)
+    threads = oracle_max_threads()
+    if w.packed:
+        rec = packed_cpu_baseline(w, d, budget_s, threads)
+        rec["host"] = host_cpu()
+        return rec
+    BH = w.batch * w.nheads
+    all_pairs = [(b, h) for b in range(w.batch) for h in range(w.nheads)]
+    # probe: one sequence per thread, spread over the workload
+    n = min(BH, threads)
+    stride = max(1, BH // n)
+    t_probe, _ = _time_pairs(ssd_recurrence_f32, d, all_pairs[::stride][:n], threads, 0.0)
+    share = 0.5 * budget_s                   # fp32 at full width; the rest below
+    rounds = max(1, int(share / max(t_probe, 1e-9)))
+    n_pairs = min(BH, rounds * n)
+    pairs = all_pairs[::max(1, BH // n_pairs)][:n_pairs]
+    t32, reps32 = _time_pairs(ssd_recurrence_f32, d, pairs, threads, share)
+    t64, reps64 = _time_pairs(ssd_recurrence, d, pairs, threads, 0.25 * budget_s)
+    scale = BH / len(pairs)
+    # one thread: this workload (one sequence) and the tiny workload (whole)
+    one = {}
+    t1, _ = _time_pairs(ssd_recurrence_f32, d, all_pairs[:1], 1, 0.1 * budget_s)
+    one[w.name] = w.tokens / (t1 * BH)
+    tw = WORKLOADS["tiny"]
+    dt_ = make_inputs(tw)
+    tt, _ = _time_pairs(ssd_recurrence_f32, dt_, None, 1, 0.05 * budget_s)
+    one["tiny"] = tw.tokens / tt
+    return {"value": w.tokens / (t32 * scale), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(pairs)} of {BH} (b,h) sequences of the {w.shape_str()} workload "
+                      f"through the oracle's token recurrence in fp32 (its float instance), "
+                      f"{reps32} repetition(s) on {threads} OpenMP threads; scaled to the whole "
+                      f"workload",
+            "fp64_value": w.tokens / (t64 * scale), "fp64_reps": reps64,
+            "one_thread_fp32": one, "host": host_cpu()}
 
 
 def copy_calibration(mb: int, dev: str) -> None:
@@ -544,8 +597,9 @@ def main(argv=None):
     ap.add_argument("--mma", default="f16", choices=["f16", "f32"])
     ap.add_argument("--chunks-per-wg", type=int, default=0)
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = auto)")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="record the main kernel's HIP events on every n-th timed step")
+    ap.add_argument("--split-samples", type=int, default=20,
+                    help="calls sampled after the timed region with event pairs around the "
+                         "whole call and its main-pass kernel (the per-kernel split)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -603,38 +657,50 @@ def main(argv=None):
         calls[k % n_sets].launch(stream)
     torch.cuda.synchronize()
 
-    # The main kernel's duration comes from a HIP event pair recorded around
-    # it on every `event_every`-th timed step (each pair costs the stream
-    # about 6 us on the headline workload, so recording it on every step
-    # would slow the steps it measures).
+    # Timed region: K back-to-back calls (every launch of each call) between
+    # two HIP events on the launch stream; their mean is the GPU time of one
+    # whole call, which the roofline divides the algorithmic bytes by.
     K = args.steps
-    every = max(1, args.event_every)
-    sampled = list(range(0, K, every))
-    evs = [(ev.create(), ev.create()) for _ in sampled]
+    e0, e1 = ev.create(), ev.create()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev.record(e0, stream)
     for k in range(K):
-        c = calls[k % n_sets]
-        if k % every == 0:
-            a, b = evs[k // every]
-            c.desc.ev_main_begin, c.desc.ev_main_end = a.value, b.value
-        else:
-            c.desc.ev_main_begin = c.desc.ev_main_end = None
-        c.launch(stream)
+        calls[k % n_sets].launch(stream)
+    ev.record(e1, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    call_ms = ev.elapsed_ms(e0, e1) / K
+    ev.destroy(e0)
+    ev.destroy(e1)
+
+    # Split of a call over its kernels, outside the timed region: event pairs
+    # around whole calls and around their main-pass kernel (each pair costs
+    # the stream a few microseconds, so these samples are not the headline).
+    S = max(1, args.split_samples)
+    evs = [tuple(ev.create() for _ in range(4)) for _ in range(S)]
+    torch.cuda.synchronize()
+    for k in range(S):
+        c = calls[k % n_sets]
+        a, m0, m1, b = evs[k]
+        c.desc.ev_main_begin, c.desc.ev_main_end = m0.value, m1.value
+        ev.record(a, stream)
+        c.launch(stream)
+        ev.record(b, stream)
+    torch.cuda.synchronize()
     for c in calls:
         c.desc.ev_main_begin = c.desc.ev_main_end = None
-    main_ms = [ev.elapsed_ms(a, b) for a, b in evs]
-    for a, b in evs:
-        ev.destroy(a)
-        ev.destroy(b)
+    main_ms = [ev.elapsed_ms(m0, m1) for _, m0, m1, _ in evs]
+    pre_ms = [ev.elapsed_ms(a, m0) for a, m0, _, _ in evs]
+    for e in evs:
+        for x in e:
+            ev.destroy(x)
 
     ms_per_step = wall / K * 1e3
     tok_s = w.tokens / (wall / K)
-    main_mean = sum(main_ms) / len(main_ms)
-    achieved = abytes / (main_mean * 1e-3) / 1e9
+    achieved = abytes / (call_ms * 1e-3) / 1e9
     flops = algorithmic_flops(w)
+    main_mean = sum(main_ms) / len(main_ms)
     rec = {
         "metric": METRIC,
         "value": tok_s,
@@ -655,11 +721,16 @@ def main(argv=None):
                    "seqlens": list(w.seqlens) if w.packed else None,
                    "chunks_per_wg": cpg, "chunk_groups": ngroups, "input_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
-                     "kernel": "ssd_chunk_scan_kernel", "kernel_ms": main_mean,
-                     "kernel_ms_p20_p50_p80": [quantile(main_ms, q) for q in (0.2, 0.5, 0.8)],
-                     "kernel_samples": len(main_ms),
-                     "algorithmic_bytes": abytes},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name, "ssd_fwd"),
+                     "kernel": "ssd_fwd (every kernel of one call: " + kernel_list(ngroups) + ")",
+                     "kernel_ms": call_ms,
+                     "algorithmic_bytes": abytes,
+                     "split": {"samples": S,
+                               "main_kernel": "ssd_chunk_scan_kernel",
+                               "main_ms_p20_p50_p80": [quantile(main_ms, q) for q in (0.2, 0.5, 0.8)],
+                               "main_hbm_frac": abytes / (main_mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "before_main_ms_p50": quantile(pre_ms, 0.5)}},
         "path": {"ms": ms_per_step, "gbs": abytes / (wall / K) / 1e9,
                  "hbm_frac": abytes / (wall / K) / 1e9 / HBM_PEAK_GBS,
                  "tflops": flops / (wall / K) / 1e12},

@@ -6,7 +6,9 @@ its Python binding) never does, and shares no code with it.
 
 Contents
   recurrence : ``ssd_recurrence`` -- the token-by-token recurrence in plain C
-               (fp64), the definition every other result is checked against.
+               (fp64), the definition every other result is checked against;
+               ``ssd_recurrence_f32``, its float instance, is the CPU
+               baseline the benchmark times (not a parity reference).
   forms      : two independent restatements used to pin the recurrence --
                the quadratic semiseparable-matrix form and the four-stage
                chunked form -- plus the A = 0 closed form.
@@ -26,7 +28,8 @@ Parity status: every function here is pinned by ``tests/test_oracle.py``,
 (hand-derived golden values, closed forms, cross-form equality and
 invariants); none is "parity unpinned".
 """
-from .recurrence import ssd_recurrence, build_oracle, oracle_max_threads  # noqa: F401
+from .recurrence import (ssd_recurrence, ssd_recurrence_f32, build_oracle,  # noqa: F401
+                         oracle_max_threads)
 from .forms import (ssd_quadratic, ssd_chunked, ssd_linear_attention_closed_form,  # noqa: F401
                     discretize)
 from .rmsnorm import rmsnorm_gated  # noqa: F401

@@ -42,6 +42,10 @@ def _load():
         lib.ssd_oracle_f64.argtypes = [i64] * 6 + [dp] * 9 + [c_int, c_dbl, c_dbl, dp, i64,
                                                                dp, dp, c_int]
         lib.ssd_oracle_f64.restype = c_int
+        f32 = ctypes.c_float
+        lib.ssd_oracle_f32.argtypes = [i64] * 6 + [dp] * 9 + [c_int, f32, f32, dp, i64,
+                                                               dp, dp, c_int]
+        lib.ssd_oracle_f32.restype = c_int
         lib.ssd_oracle_max_threads.argtypes = []
         lib.ssd_oracle_max_threads.restype = c_int
         _lib = lib
@@ -101,4 +105,42 @@ def ssd_recurrence(x, dt, A, B, C, D=None, z=None, dt_bias=None, initial_states=
                                 pp, npairs, _ptr(out), _ptr(fin), int(nthreads))
     if rc != 0:
         raise ValueError(f"ssd_oracle_f64 failed with code {rc}")
+    return out, fin
+
+
+def _f32(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        import torch
+        a = a.detach().to("cpu", torch.float32).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def ssd_recurrence_f32(x, dt, A, B, C, D=None, z=None, dt_bias=None, initial_states=None,
+                       dt_softplus: bool = False,
+                       dt_limit: Tuple[float, float] = (0.0, math.inf),
+                       pairs: Optional[Sequence[Tuple[int, int]]] = None,
+                       nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """The same token recurrence in single precision (the C function's float
+    instance).  Not a parity reference: the benchmark times it as the CPU
+    baseline.  Arguments and results as ``ssd_recurrence``, in float32."""
+    x, dt, A, B, C = (_f32(v) for v in (x, dt, A, B, C))
+    D, z, dt_bias, h0 = (_f32(v) for v in (D, z, dt_bias, initial_states))
+    Bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    fill = np.nan if pairs is not None else 0.0
+    out = np.full((Bsz, L, H, P), fill, dtype=np.float32)
+    fin = np.full((Bsz, H, P, N), fill, dtype=np.float32)
+    if pairs is not None:
+        parr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
+        pp, npairs = _ptr(parr), parr.shape[0]
+    else:
+        pp, npairs = None, 0
+    rc = _load().ssd_oracle_f32(Bsz, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0),
+                                int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]),
+                                pp, npairs, _ptr(out), _ptr(fin), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"ssd_oracle_f32 failed with code {rc}")
     return out, fin

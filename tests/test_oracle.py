@@ -264,3 +264,19 @@ def test_tail_padding_is_inert():
         np.testing.assert_allclose(c_out, out, rtol=1e-11, atol=1e-11)
         np.testing.assert_allclose(c_fin, fin, rtol=1e-11, atol=1e-11)
         assert np.all(inter["delta"].reshape(1, 2, -1)[:, :, 45:] == 0)
+
+
+def test_float_instance_is_the_same_recurrence():
+    """The fp32 instance the benchmark times as its CPU baseline follows the
+    fp64 recurrence to single-precision rounding (every option on)."""
+    from oracle import ssd_recurrence_f32
+    d = random_inputs(2, 150, 4, 8, 16, 2, seed=77, has_D=True, has_z=True, has_h0=True,
+                      dt_bias=True)
+    kw = dict(D=d["D"], z=d["z"], dt_bias=d["dt_bias"], initial_states=d["initial_states"],
+              dt_softplus=True, dt_limit=(0.7, 1.2))
+    ref = ssd_recurrence(d["x"], d["dt"], d["A"], d["B"], d["C"], **kw)
+    for threads in (1, 0):
+        got = ssd_recurrence_f32(d["x"], d["dt"], d["A"], d["B"], d["C"], nthreads=threads, **kw)
+        for g, r in zip(got, ref):
+            assert g.dtype == np.float32
+            assert np.abs(g - r).max() <= 1e-5 * np.abs(r).max()
