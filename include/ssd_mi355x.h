@@ -168,6 +168,31 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A,
                    void *out, float *final_state, void *stream,
                    const ssd_desc *d);
 
+/* Largest workspace, in bytes, that ssd_fwd_noalloc serves from its static
+ * scratch (compare ssd_fwd_workspace_size against it). */
+#define SSD_FWD_NOALLOC_MAX_SCRATCH ((size_t)64 << 20)
+
+/* ssd_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments and results as ssd_fwd, but the plan's
+ * workspace is a static device array inside the library (one per GPU, held
+ * until the process ends) instead of desc->workspace, which is ignored.  The
+ * call allocates and frees nothing; on its first call on a device it looks
+ * up that device's scratch address (hipGetSymbolAddress), so that device
+ * must be current and the stream must belong to it.
+ * Limits and errors as ssd_fwd, plus: SSD_ERR_WORKSPACE when the plan needs
+ * more than SSD_FWD_NOALLOC_MAX_SCRATCH bytes (checked before any device
+ * call); SSD_ERR_INVALID_ARG when the stream is not on the current device;
+ * SSD_ERR_LAUNCH when the runtime cannot give the scratch address.  Every
+ * call on one GPU shares its scratch, so calls that overlap on one GPU (on
+ * different streams) race and must be serialised by the caller; nothing in
+ * the scratch needs to start at zero. */
+ssd_status ssd_fwd_noalloc(const void *x, const float *dt, const float *A,
+                           const void *B, const void *C, const float *D,
+                           int64_t chunk, int dt_softplus, int return_final_state,
+                           void *out, float *final_state, void *stream,
+                           const ssd_desc *d);
+
 /* Bytes of device workspace ssd_bwd needs for this descriptor (the state
  * entering every chunk, per-head dB and dC, per-row partial sums).  Errors as
  * ssd_bwd's validation of shapes and codes. */

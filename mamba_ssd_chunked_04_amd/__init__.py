@@ -4,9 +4,11 @@ The compute path is the HIP library libssd_mi355x.so (C ABI in
 include/ssd_mi355x.h); this package only binds it.  PyTorch supplies device
 memory and streams.
 """
-from .binding import (EXPORTED_SYMBOLS, SsdCall, SsdDesc, SsdError, load_library,  # noqa: F401
-                      make_desc, plan, prepare, prepare_bwd, rmsnorm_gated, causal_conv1d,
-                      ssd_bwd, ssd_fwd, status_str, workspace_size)
+from .binding import (EXPORTED_SYMBOLS, NOALLOC_MAX_SCRATCH, SSD_ERR_WORKSPACE,  # noqa: F401
+                      SsdCall, SsdDesc, SsdError, load_library, make_desc, plan, prepare,
+                      prepare_bwd, rmsnorm_gated, causal_conv1d, ssd_bwd, ssd_fwd, status_str,
+                      workspace_size)
 
 __all__ = ["ssd_fwd", "ssd_bwd", "prepare_bwd", "rmsnorm_gated", "causal_conv1d", "prepare", "plan", "workspace_size", "load_library", "make_desc",
-           "SsdCall", "SsdDesc", "SsdError", "status_str", "EXPORTED_SYMBOLS"]
+           "SsdCall", "SsdDesc", "SsdError", "status_str", "EXPORTED_SYMBOLS",
+           "NOALLOC_MAX_SCRATCH", "SSD_ERR_WORKSPACE"]

@@ -19,8 +19,10 @@ SSD_MMA_F16, SSD_MMA_F32 = 0, 2
 
 # Every symbol include/ssd_mi355x.h declares.
 EXPORTED_SYMBOLS = ("ssd_desc_init", "ssd_fwd_workspace_size", "ssd_fwd_plan", "ssd_fwd",
-                    "ssd_bwd_workspace_size", "ssd_bwd", "ssd_rmsnorm_gated", "ssd_causal_conv1d",
-                    "ssd_status_str", "ssd_abi_version")
+                    "ssd_fwd_noalloc", "ssd_bwd_workspace_size", "ssd_bwd", "ssd_rmsnorm_gated",
+                    "ssd_causal_conv1d", "ssd_status_str", "ssd_abi_version")
+# include/ssd_mi355x.h: SSD_FWD_NOALLOC_MAX_SCRATCH
+NOALLOC_MAX_SCRATCH = 64 << 20
 
 
 class SsdDesc(ctypes.Structure):
@@ -69,6 +71,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ssd_fwd_plan.restype = c_int
     lib.ssd_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, c_int, c_int, vp, vp, vp, dp]
     lib.ssd_fwd.restype = c_int
+    lib.ssd_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, c_int, c_int, vp, vp, vp, dp]
+    lib.ssd_fwd_noalloc.restype = c_int
     lib.ssd_rmsnorm_gated.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_float, vp, vp]
     lib.ssd_rmsnorm_gated.restype = c_int
     lib.ssd_bwd_workspace_size.argtypes = [dp, i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -138,17 +142,30 @@ class SsdCall:
     stream handle (an int from ``torch.cuda.Stream.cuda_stream``).
     """
 
-    def __init__(self, args, desc: SsdDesc, keep, error_flag=None):
+    def __init__(self, args, desc: SsdDesc, keep, error_flag=None, noalloc: bool = False):
         self._args = args
         self.desc = desc
         self._keep = keep        # tensors whose storage the pointers refer to
         self.error_flag = error_flag   # packed calls: the device flag the kernels set
+        self.noalloc = noalloc   # launch through ssd_fwd_noalloc
 
     def launch(self, stream: int) -> None:
+        if self.noalloc:
+            self.launch_noalloc(stream)
+            return
         a = self._args
         st = load_library().ssd_fwd(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9],
                                     a[10], ctypes.c_void_p(stream), ctypes.byref(self.desc))
         _raise_for(st, "ssd_fwd")
+
+    def launch_noalloc(self, stream: int) -> None:
+        """The same call through ``ssd_fwd_noalloc`` (the library's static
+        scratch instead of this call's workspace, which is not read)."""
+        a = self._args
+        st = load_library().ssd_fwd_noalloc(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8],
+                                            a[9], a[10], ctypes.c_void_p(stream),
+                                            ctypes.byref(self.desc))
+        _raise_for(st, "ssd_fwd_noalloc")
 
     def check(self) -> None:
         """Packed calls: synchronise and raise ValueError if any launch of this
@@ -168,8 +185,12 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
             dt_softplus: bool = False, dt_limit: Tuple[float, float] = (0.0, math.inf),
             return_final_state: bool = False, mma: str = "f16", out_dtype=None,
             chunks_per_wg: int = 0, out=None, final_state=None, workspace=None,
-            cu_seqlens=None, max_seqlen: Optional[int] = None):
+            cu_seqlens=None, max_seqlen: Optional[int] = None, noalloc: bool = False):
     """Validate torch tensors, allocate outputs/workspace, and build an SsdCall.
+
+    With ``noalloc`` no workspace is allocated and the call launches through
+    ``ssd_fwd_noalloc`` (the library's static scratch; ValueError from the
+    launch when the plan needs more than NOALLOC_MAX_SCRATCH bytes).
 
     ``out`` is float32 unless ``out_dtype`` (float32 or bfloat16) says
     otherwise, whatever the dtype of x, B and C.
@@ -249,7 +270,7 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     desc.z, desc.dt_bias, desc.initial_state = _ptr(z), _ptr(dt_bias), _ptr(initial_states)
     desc.chunks_per_wg = int(chunks_per_wg)
     nbytes = workspace_size(desc, chunk_size)
-    if nbytes > 0 and workspace is None:
+    if nbytes > 0 and workspace is None and not noalloc:
         workspace = torch.empty(nbytes, device=dev, dtype=torch.uint8)
     if workspace is not None:
         desc.workspace, desc.workspace_bytes = workspace.data_ptr(), workspace.numel()
@@ -258,7 +279,7 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
             _ptr(final_state) if return_final_state else None)
     keep = (x, dt, A, B, C, D, z, dt_bias, initial_states, out, final_state, workspace, cu_seqlens,
             error_flag)
-    return (SsdCall(args, desc, keep, error_flag), out,
+    return (SsdCall(args, desc, keep, error_flag, noalloc=noalloc), out,
             (final_state if return_final_state else None), workspace)
 
 
@@ -266,7 +287,7 @@ def ssd_fwd(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
             dt_softplus: bool = False, dt_limit: Tuple[float, float] = (0.0, math.inf),
             return_final_state: bool = False, mma: str = "f16", out_dtype=None,
             chunks_per_wg: int = 0, cu_seqlens=None, max_seqlen: Optional[int] = None,
-            check_offsets: bool = True):
+            check_offsets: bool = True, noalloc: bool = False):
     """SSD chunked forward on the current torch stream.
 
     Returns ``out`` or ``(out, final_state)`` when ``return_final_state``.
@@ -276,14 +297,16 @@ def ssd_fwd(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     was longer than it (or the offsets were malformed).  Pass
     ``check_offsets=False`` to skip that synchronisation (then nothing
     reports such offsets; ``prepare`` and ``call.check()`` give control over
-    when the check runs).
+    when the check runs).  ``noalloc`` runs it through ``ssd_fwd_noalloc``
+    (no workspace; the outputs are still allocated here unless the caller
+    uses ``prepare`` with its own).
     """
     import torch
     call, out, fin, _ws = prepare(x, dt, A, B, C, chunk_size, D=D, z=z, dt_bias=dt_bias,
                                   initial_states=initial_states, dt_softplus=dt_softplus,
                                   dt_limit=dt_limit, return_final_state=return_final_state,
                                   mma=mma, out_dtype=out_dtype, chunks_per_wg=chunks_per_wg,
-                                  cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
+                                  cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, noalloc=noalloc)
     with torch.cuda.device(x.device):
         call.launch(torch.cuda.current_stream(x.device).cuda_stream)
         if cu_seqlens is not None and max_seqlen is not None and check_offsets:

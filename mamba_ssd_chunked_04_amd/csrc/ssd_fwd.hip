@@ -39,6 +39,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "../../include/ssd_mi355x.h"
 
@@ -1307,6 +1308,96 @@ ssd_status dispatch_n(const Params &prm, const Plan &pl, hipStream_t s, const ss
   return dispatch_mma<Q, 128>(prm, pl, s, d);
 }
 
+// The forward with its workspace given explicitly (the caller's buffer, or
+// the static scratch of ssd_fwd_noalloc); `d->workspace` is not read here.
+ssd_status fwd_impl(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                    const float *D, int64_t chunk, int dt_softplus, int return_final_state,
+                    void *out, float *final_state, void *stream, const ssd_desc *d, void *ws,
+                    size_t ws_bytes) {
+  const ssd_status st = check_shape(d, chunk);
+  if (st != SSD_OK) return st;
+  if (!x || !dt || !A || !B || !C || !out) return SSD_ERR_INVALID_ARG;
+  if (return_final_state && !final_state) return SSD_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(out) ||
+      (d->z && !aligned16(d->z)) || !aligned16(dt) ||
+      (d->initial_state && !aligned16(d->initial_state)) ||
+      (return_final_state && !aligned16(final_state)) ||
+      ((uintptr_t)d->cu_seqlens & 3u) != 0 || ((uintptr_t)d->error_flag & 3u) != 0)
+    return SSD_ERR_INVALID_ARG;
+  const Plan pl = make_plan(d, chunk);
+  const size_t need = pl.total();
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return SSD_ERR_WORKSPACE;
+
+  Params prm;
+  memset(&prm, 0, sizeof(prm));
+  prm.x = x;
+  prm.dt = dt;
+  prm.A = A;
+  prm.B = B;
+  prm.C = C;
+  prm.D = D;
+  prm.z = d->z;
+  prm.dt_bias = d->dt_bias;
+  prm.h0 = d->initial_state;
+  prm.out = out;
+  prm.final_state = final_state;
+  char *wsc = static_cast<char *>(ws);
+  prm.grp_state = pl.state_bytes ? reinterpret_cast<float *>(wsc) : nullptr;
+  prm.grp_lam = pl.lam_bytes ? reinterpret_cast<float *>(wsc + pl.state_bytes) : nullptr;
+  prm.cu_seqlens = d->cu_seqlens;
+  prm.error_flag = d->cu_seqlens ? d->error_flag : nullptr;
+  prm.packed_tokens = d->cu_seqlens ? d->packed_tokens : 0;
+  prm.batch = d->batch;
+  prm.L = d->seqlen;
+  prm.Q = (int)chunk;
+  prm.H = d->nheads;
+  prm.G = d->ngroups;
+  prm.nc = pl.nc;
+  prm.ngroups = pl.ngroups;
+  prm.cpg = pl.cpg;
+  prm.dt_min = d->dt_min;
+  prm.dt_max = d->dt_max;
+  prm.dt_softplus = dt_softplus ? 1 : 0;
+  prm.z_bf16 = d->z_dtype == SSD_BF16;
+  prm.out_bf16 = d->out_dtype == SSD_BF16;
+  prm.ret_final = return_final_state ? 1 : 0;
+  prm.chained = pl.ngroups - 1 > kFoldGroups;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (chunk) {
+    case 64: return dispatch_n<64>(prm, pl, s, d);
+    case 128: return dispatch_n<128>(prm, pl, s, d);
+    default: return dispatch_n<256>(prm, pl, s, d);
+  }
+}
+
+// Scratch of ssd_fwd_noalloc: the group states and decays that ssd_fwd keeps
+// in the caller's workspace, in a file-scope device array instead (every GPU
+// the library runs on holds its own copy until the process ends).  In host
+// code `scratch` only names the symbol; its device address on each GPU comes
+// from hipGetSymbolAddress, taken once per device and kept in scratch_ptr.
+constexpr size_t kScratchBytes = SSD_FWD_NOALLOC_MAX_SCRATCH;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void *ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot scratch_slots[kMaxDevices];
+
+// Device address of `scratch` on `dev` (which must be the current device),
+// or NULL if the runtime cannot give it.
+void *scratch_ptr(int dev) {
+  ScratchSlot &s = scratch_slots[dev];
+  std::call_once(s.once, [&s] {
+    s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch));
+    if (s.err != hipSuccess) s.ptr = nullptr;
+  });
+  return s.ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1351,62 +1442,31 @@ ssd_status ssd_fwd_plan(const ssd_desc *d, int64_t chunk, int64_t *chunks_per_wg
 ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B, const void *C,
                    const float *D, int64_t chunk, int dt_softplus, int return_final_state,
                    void *out, float *final_state, void *stream, const ssd_desc *d) {
+  if (!d) return SSD_ERR_INVALID_ARG;
+  return fwd_impl(x, dt, A, B, C, D, chunk, dt_softplus, return_final_state, out, final_state,
+                  stream, d, d->workspace, d->workspace_bytes);
+}
+
+ssd_status ssd_fwd_noalloc(const void *x, const float *dt, const float *A, const void *B,
+                           const void *C, const float *D, int64_t chunk, int dt_softplus,
+                           int return_final_state, void *out, float *final_state, void *stream,
+                           const ssd_desc *d) {
+  // everything that needs no device first, so a refused call touches no GPU
   const ssd_status st = check_shape(d, chunk);
   if (st != SSD_OK) return st;
-  if (!x || !dt || !A || !B || !C || !out) return SSD_ERR_INVALID_ARG;
-  if (return_final_state && !final_state) return SSD_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(out) ||
-      (d->z && !aligned16(d->z)) || !aligned16(dt) ||
-      (d->initial_state && !aligned16(d->initial_state)) ||
-      (return_final_state && !aligned16(final_state)) ||
-      ((uintptr_t)d->cu_seqlens & 3u) != 0 || ((uintptr_t)d->error_flag & 3u) != 0)
-    return SSD_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, chunk);
-  const size_t need = pl.total();
-  if (need > 0 && (!d->workspace || d->workspace_bytes < need || !aligned16(d->workspace)))
-    return SSD_ERR_WORKSPACE;
-
-  Params prm;
-  memset(&prm, 0, sizeof(prm));
-  prm.x = x;
-  prm.dt = dt;
-  prm.A = A;
-  prm.B = B;
-  prm.C = C;
-  prm.D = D;
-  prm.z = d->z;
-  prm.dt_bias = d->dt_bias;
-  prm.h0 = d->initial_state;
-  prm.out = out;
-  prm.final_state = final_state;
-  char *ws = static_cast<char *>(d->workspace);
-  prm.grp_state = pl.state_bytes ? reinterpret_cast<float *>(ws) : nullptr;
-  prm.grp_lam = pl.lam_bytes ? reinterpret_cast<float *>(ws + pl.state_bytes) : nullptr;
-  prm.cu_seqlens = d->cu_seqlens;
-  prm.error_flag = d->cu_seqlens ? d->error_flag : nullptr;
-  prm.packed_tokens = d->cu_seqlens ? d->packed_tokens : 0;
-  prm.batch = d->batch;
-  prm.L = d->seqlen;
-  prm.Q = (int)chunk;
-  prm.H = d->nheads;
-  prm.G = d->ngroups;
-  prm.nc = pl.nc;
-  prm.ngroups = pl.ngroups;
-  prm.cpg = pl.cpg;
-  prm.dt_min = d->dt_min;
-  prm.dt_max = d->dt_max;
-  prm.dt_softplus = dt_softplus ? 1 : 0;
-  prm.z_bf16 = d->z_dtype == SSD_BF16;
-  prm.out_bf16 = d->out_dtype == SSD_BF16;
-  prm.ret_final = return_final_state ? 1 : 0;
-  prm.chained = pl.ngroups - 1 > kFoldGroups;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (chunk) {
-    case 64: return dispatch_n<64>(prm, pl, s, d);
-    case 128: return dispatch_n<128>(prm, pl, s, d);
-    default: return dispatch_n<256>(prm, pl, s, d);
-  }
+  if (pl.total() > kScratchBytes) return SSD_ERR_WORKSPACE;
+  if (!x || !dt || !A || !B || !C || !out) return SSD_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_LAUNCH;
+  hipDevice_t sdev = -1;
+  if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+    return SSD_ERR_INVALID_ARG;
+  if ((int)sdev != dev) return SSD_ERR_INVALID_ARG;  // the scratch address is per device
+  void *ws = pl.total() > 0 ? scratch_ptr(dev) : nullptr;
+  if (pl.total() > 0 && !ws) return SSD_ERR_LAUNCH;
+  return fwd_impl(x, dt, A, B, C, D, chunk, dt_softplus, return_final_state, out, final_state,
+                  stream, d, ws, kScratchBytes);
 }
 
 const char *ssd_status_str(int status) {

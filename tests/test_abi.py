@@ -295,3 +295,24 @@ def test_product_path_does_not_touch_oracle():
         if os.path.isfile(path) and path.endswith((".py", ".hip", ".h", ".cpp")):
             src = open(path, encoding="utf-8").read()
             assert "oracle" not in src.lower(), path
+
+
+def test_noalloc_refuses_large_plans_before_touching_a_device(lib):
+    """ssd_fwd_noalloc checks the plan against its static scratch first, so a
+    plan that needs more is refused with SSD_ERR_WORKSPACE on any host."""
+    d = bnd.make_desc(1, 100000, 8, 64, 128, 1)
+    d.chunks_per_wg = 1
+    assert bnd.workspace_size(d, 64) > bnd.NOALLOC_MAX_SCRATCH
+    rc = lib.ssd_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 1, 0, FAKE, None, None,
+                             ctypes.byref(d))
+    assert rc == bnd.SSD_ERR_WORKSPACE
+    # shape errors come first, as for ssd_fwd
+    d2 = bnd.make_desc(1, 64, 3, 64, 64, 2)          # H % G != 0
+    assert lib.ssd_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 1, 0, FAKE, None, None,
+                               ctypes.byref(d2)) == bnd.SSD_ERR_INVALID_ARG
+
+
+def test_noalloc_limit_matches_the_header():
+    src = open(os.path.join(ROOT, "include", "ssd_mi355x.h")).read()
+    m = re.search(r"#define SSD_FWD_NOALLOC_MAX_SCRATCH \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == bnd.NOALLOC_MAX_SCRATCH
