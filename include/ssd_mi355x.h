@@ -60,9 +60,14 @@ typedef enum { SSD_F32 = 0, SSD_F16 = 1, SSD_BF16 = 2 } ssd_dtype;
 /* Matrix-core operand precision.  SSD_MMA_F16: x, B, C, the masked C.B^T
  * weights, the decay-weighted B and the carried state are rounded to fp16
  * for the MFMA products, accumulating in fp32 (the mixed precision the page
- * "Mamba-2 SSD for Ascend NPU" describes for its Cube units).  SSD_MMA_F32:
- * every operand stays fp32 (a slower check path). */
-typedef enum { SSD_MMA_F16 = 0, SSD_MMA_F32 = 2 } ssd_mma;
+ * "Mamba-2 SSD for Ascend NPU" describes for its Cube units); every operand
+ * must then lie in fp16's range (|v| <= 65504; magnitudes below about 6e-5
+ * lose precision and below 6e-8 flush to zero), so fp32 or bf16 inputs
+ * outside it overflow to inf or vanish.  SSD_MMA_BF16: the same operands
+ * rounded to bf16 (fp32's exponent range, 8 significant bits), the precision
+ * that page lists as its next extension ("Limitations and roadmap").
+ * SSD_MMA_F32: every operand stays fp32 (a slower check path). */
+typedef enum { SSD_MMA_F16 = 0, SSD_MMA_BF16 = 1, SSD_MMA_F32 = 2 } ssd_mma;
 
 /* Shape, dtypes and optional inputs of one call. */
 typedef struct ssd_desc {
@@ -72,7 +77,7 @@ typedef struct ssd_desc {
   int64_t headdim;   /* P  == 64 */
   int64_t dstate;    /* N  in {64, 128} */
   int64_t ngroups;   /* G  >= 1, H % G == 0; head h reads B/C group h/(H/G) */
-  int32_t x_dtype;   /* dtype of x, B and C: SSD_F32 or SSD_BF16 */
+  int32_t x_dtype;   /* dtype of x: SSD_F32 or SSD_BF16 */
   int32_t z_dtype;   /* dtype of z: SSD_F32 or SSD_BF16 (ignored when z NULL) */
   int32_t out_dtype; /* dtype of out: SSD_F32 or SSD_BF16 */
   int32_t mma;       /* ssd_mma */
@@ -89,7 +94,7 @@ typedef struct ssd_desc {
   size_t workspace_bytes;    /* its size; see ssd_fwd_workspace_size          */
   int32_t chunks_per_wg;     /* chunks one workgroup walks in sequence; 0 picks
                                 automatically (see ssd_fwd_plan)              */
-  int32_t reserved;          /* must be 0 */
+  int32_t bc_dtype;          /* dtype of B and C: SSD_F32 or SSD_BF16       */
   void *ev_main_begin;       /* optional hipEvent_t (as void*) recorded on the
                                 stream right before the main-pass kernel, for
                                 measurement; NULL records nothing             */
@@ -134,8 +139,9 @@ typedef struct ssd_desc {
                                 dense calls                               */
 } ssd_desc;
 
-/* Fills `d` with defaults for the given shape: fp32 storage, fp16 MMA, no
- * optional inputs, no dt_limit, automatic plan, no workspace. */
+/* Fills `d` with defaults for the given shape: fp32 storage (x, B, C, z,
+ * out), fp16 MMA, no optional inputs, no dt_limit, automatic plan, no
+ * workspace. */
 void ssd_desc_init(ssd_desc *d, int64_t batch, int64_t seqlen, int64_t nheads,
                    int64_t headdim, int64_t dstate, int64_t ngroups);
 
@@ -277,7 +283,7 @@ const char *ssd_status_str(int status);
 /* ABI version of this header (bumped on any incompatible change). */
 int ssd_abi_version(void);
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,7 @@ from .build import LIB
 
 SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_LAUNCH = range(5)
 SSD_F32, SSD_F16, SSD_BF16 = 0, 1, 2
-SSD_MMA_F16, SSD_MMA_F32 = 0, 2
+SSD_MMA_F16, SSD_MMA_BF16, SSD_MMA_F32 = 0, 1, 2
 
 # Every symbol include/ssd_mi355x.h declares.
 EXPORTED_SYMBOLS = ("ssd_desc_init", "ssd_fwd_workspace_size", "ssd_fwd_plan", "ssd_fwd",
@@ -35,7 +35,7 @@ class SsdDesc(ctypes.Structure):
         ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
         ("z", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-        ("chunks_per_wg", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("chunks_per_wg", ctypes.c_int32), ("bc_dtype", ctypes.c_int32),
         ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p),
         ("cu_seqlens", ctypes.c_void_p), ("packed_tokens", ctypes.c_int64),
         ("error_flag", ctypes.c_void_p),
@@ -235,8 +235,8 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
         row_len = max(1, int(max_seqlen))
     if dt.shape != (Bsz, L, H) or A.shape != (H,) or B.shape != (Bsz, L, G, N) or C.shape != B.shape:
         raise ValueError("shape mismatch: x[B,L,H,P], dt[B,L,H], A[H], B/C[B,L,G,N]")
-    if B.dtype != x.dtype or C.dtype != x.dtype:
-        raise ValueError("x, B and C must share one dtype")
+    if C.dtype != B.dtype:
+        raise ValueError("B and C must share one dtype")
     for name, t in (("dt", dt), ("A", A), ("D", D), ("dt_bias", dt_bias),
                     ("initial_states", initial_states)):
         if t is not None and t.dtype != torch.float32:
@@ -263,9 +263,12 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
         error_flag = torch.zeros(1, device=dev, dtype=torch.int32)
         desc.error_flag = error_flag.data_ptr()
     desc.x_dtype = _dtype_code(x.dtype)
+    desc.bc_dtype = _dtype_code(B.dtype)
     desc.z_dtype = _dtype_code(z.dtype) if z is not None else SSD_F32
     desc.out_dtype = _dtype_code(out.dtype)
-    desc.mma = {"f16": SSD_MMA_F16, "f32": SSD_MMA_F32}[mma]
+    if mma not in ("f16", "bf16", "f32"):
+        raise ValueError(f"mma must be 'f16', 'bf16' or 'f32', got {mma!r}")
+    desc.mma = {"f16": SSD_MMA_F16, "bf16": SSD_MMA_BF16, "f32": SSD_MMA_F32}[mma]
     desc.dt_min, desc.dt_max = float(dt_limit[0]), float(dt_limit[1])
     desc.z, desc.dt_bias, desc.initial_state = _ptr(z), _ptr(dt_bias), _ptr(initial_states)
     desc.chunks_per_wg = int(chunks_per_wg)

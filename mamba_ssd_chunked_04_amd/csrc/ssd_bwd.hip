@@ -721,9 +721,12 @@ ssd_status check_bwd(const ssd_desc *d, int64_t chunk) {
   if (d->batch < 1 || d->seqlen < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
       d->ngroups < 1 || chunk < 1 || d->nheads % d->ngroups != 0)
     return SSD_ERR_INVALID_ARG;
-  if (!(d->dt_min <= d->dt_max) || d->reserved != 0) return SSD_ERR_INVALID_ARG;
+  if (!(d->dt_min <= d->dt_max)) return SSD_ERR_INVALID_ARG;
+  if (d->bc_dtype != SSD_F32 && d->bc_dtype != SSD_BF16 && d->bc_dtype != SSD_F16)
+    return SSD_ERR_INVALID_ARG;
   if (d->headdim != kP || d->dstate != kN || chunk != kQ) return SSD_ERR_UNSUPPORTED;
-  if (d->x_dtype != SSD_F32 || (d->z && d->z_dtype != SSD_F32) || d->cu_seqlens)
+  if (d->x_dtype != SSD_F32 || d->bc_dtype != SSD_F32 || (d->z && d->z_dtype != SSD_F32) ||
+      d->cu_seqlens)
     return SSD_ERR_UNSUPPORTED;
   // 32-bit byte offsets within one batch row, 32-bit grid
   if (d->seqlen * d->nheads * kP * 4 >= ((int64_t)1 << 31) || d->batch * d->nheads >= ((int64_t)1 << 31))

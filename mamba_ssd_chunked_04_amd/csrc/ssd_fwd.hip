@@ -1,1160 +1,11 @@
-// Mamba-2 SSD chunked forward for MI355X (gfx950, CDNA4): HIP kernels and the
-// C ABI declared in include/ssd_mi355x.h.
-//
-// The chunked algorithm follows page "ops-transformer MambaV2 算子套件", §1.3
-// (intra-chunk matrix products plus an inter-chunk state recurrence) and the
-// operator chain of its §2 / §4.2-§4.5:
-//   chunk_cumsum   delta = clamp(softplus(dt + dt_bias)), Lam = in-chunk
-//                  inclusive prefix of delta*A, Lam_end = its last value
-//   chunk_state    S_loc = sum_i exp(Lam_end - Lam_i) delta_i x_i (outer) B_i
-//   state_passing  S_in[c+1] = exp(Lam_end[c]) S_in[c] + S_loc[c]
-//   chunk_scan     y_i = sum_{j<=i} (C_i.B_j) exp(Lam_i - Lam_j) delta_j x_j
-//                        + exp(Lam_i) C_i . S_in[c]  + D x_i,  then * silu(z_i)
-//
-// MI355X design (not the Ascend Cube/Vector split of the pages):
-//   * one workgroup (4 or 8 wave64s) walks `cpg` consecutive chunks of one
-//     (b, h), keeping the P x N state in MFMA accumulators across chunks, so
-//     the state recurrence costs no HBM traffic inside a chunk group;
-//   * chunk_cumsum runs inside the matrix passes, at the start of each chunk;
-//   * when (b, h) pairs alone cannot fill 256 CUs, the sequence is cut into
-//     chunk groups: a first pass (ssd_group_state_kernel) builds each
-//     group's state from zero, and the main pass (ssd_chunk_scan_kernel)
-//     chains the aggregates of the groups before its own (state_passing)
-//     to start every group from its entering state (with many groups a
-//     separate elementwise pass, ssd_group_passing_kernel, chains them once);
-//   * all contractions (C.B^T, M.X, C.S^T, X^T.diag(w).B) are
-//     v_mfma_f32_16x16x32_f16 tiles (or 16x16x4 fp32 on the check path) with
-//     B, X staged in LDS 64 tokens at a time and C held in registers;
-//   * the masked C.B^T block is computed transposed, so its accumulator
-//     layout is directly the A operand of the M.X product (no LDS round trip);
-//   * workgroup ids are swizzled so heads sharing a B/C group run on the same
-//     XCD (shared L2);
-//   * packed variable-length sequences (cu_seqlens) are batch rows whose
-//     token span comes from the offsets: each is chunked from its own start
-//     and its state restarts there, the form page "Mamba-2 SSD for Ascend
-//     NPU" lists under "Limitations and roadmap" (varlen, cu_seqlens).
-#include <hip/hip_runtime.h>
-
-#include <math.h>
-#include <stdint.h>
-#include <string.h>
-
+// Mamba-2 SSD chunked forward for MI355X (gfx950, CDNA4): the C ABI declared in
+// include/ssd_mi355x.h (validation, the plan, the workspace and the static
+// scratch of ssd_fwd_noalloc); the kernels are in ssd_fwd_impl.h.
 #include <mutex>
 
-#include "../../include/ssd_mi355x.h"
+#include "ssd_fwd_impl.h"
 
-namespace {
-
-constexpr int kJB = 64;         // tokens per LDS-staged block
-constexpr int kP = 64;          // compiled head dim
-constexpr float kLog2e = 1.4426950408889634f;
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-// ---------------------------------------------------------------- operand types
-template <bool F32> struct Mma;
-template <> struct Mma<false> {
-  using T = _Float16;
-  using frag = f16x8;
-  using quad = f16x4;
-};
-template <> struct Mma<true> {
-  using T = float;
-  using frag = f32x8;
-  using quad = f32x4;
-};
-
-// D += A.B over one 32-wide K block.  Lane l holds A row (l%16) and B column
-// (l%16), eight K values each (the same eight K indices in A and B), and the
-// 16x16 result rows 4*(l/16)..+3 of column l%16.
-__device__ __forceinline__ f32x4 mma(const f16x8 &a, const f16x8 &b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma(const f32x8 &a, const f32x8 &b, f32x4 c) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
-  return c;
-}
-
-__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
-
-// ---------------------------------------------------------------- buffer access
-// Every tensor of one batch row is addressed through a raw buffer resource
-// (base in SGPRs, 32-bit byte offsets per lane).  The hardware range check
-// returns zeros for loads past the end of the row's data and drops stores
-// past it, which is how tokens beyond the sequence end are handled.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) {
-  return __uint_as_float(v << 16);
-}
-
-// Round-to-nearest-even float -> bf16 bits (NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// Storage formats of x, B, C (and z).  Loads are split into an issue step
-// (raw registers) and a convert step so a whole block's loads can be in
-// flight before any of them is used.  Offsets are in elements.
-struct IoF32 {
-  static constexpr int esz = 4;
-  using raw4 = f32x4;
-  struct raw8 {
-    f32x4 lo, hi;
-  };
-  static __device__ __forceinline__ raw4 load4(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off * 4, 0, 0));
-  }
-  static __device__ __forceinline__ raw8 load8(rsrc_t r, uint32_t off) {
-    return raw8{load4(r, off), load4(r, off + 4)};
-  }
-  static __device__ __forceinline__ f32x4 cvt4(const raw4 &v) { return v; }
-  static __device__ __forceinline__ float cvt8(const raw8 &v, int e) {
-    return e < 4 ? v.lo[e] : v.hi[e - 4];
-  }
-  static __device__ __forceinline__ float load1(rsrc_t r, uint32_t off) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off * 4, 0, 0));
-  }
-};
-
-struct IoBF16 {
-  static constexpr int esz = 2;
-  typedef unsigned int raw4 __attribute__((vector_size(8)));
-  typedef unsigned int raw8 __attribute__((vector_size(16)));
-  static __device__ __forceinline__ raw4 load4(rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off * 2, 0, 0);
-  }
-  static __device__ __forceinline__ raw8 load8(rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off * 2, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 cvt4(const raw4 &v) {
-    f32x4 o;
-    o[0] = bf16_bits_to_f32(v[0] & 0xffffu);
-    o[1] = bf16_bits_to_f32(v[0] >> 16);
-    o[2] = bf16_bits_to_f32(v[1] & 0xffffu);
-    o[3] = bf16_bits_to_f32(v[1] >> 16);
-    return o;
-  }
-  static __device__ __forceinline__ float cvt8(const raw8 &v, int e) {
-    const uint32_t w = v[e >> 1];
-    return bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xffffu));
-  }
-  static __device__ __forceinline__ float load1(rsrc_t r, uint32_t off) {
-    return bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off * 2, 0, 0));
-  }
-};
-
-// ---------------------------------------------------------------- parameters
-struct Params {
-  const void *x;
-  const float *dt;
-  const float *A;
-  const void *B;
-  const void *C;
-  const float *D;
-  const void *z;
-  const float *dt_bias;
-  const float *h0;
-  void *out;
-  float *final_state;
-  float *grp_state;  // [B*H][ngroups-1][P*N]: group aggregates (state from a zero
-                     // start), or entering states once the passing pass ran
-  float *grp_lam;    // [B*H][ngroups-1]: group total log2-decay
-  const int32_t *cu_seqlens;  // packed calls: [batch+1] token offsets, else NULL
-  int32_t *error_flag;        // packed calls: set to 1 on offsets that break the contract
-  int64_t packed_tokens;      // packed calls: T when known (offsets are clamped to it), else 0
-  int64_t batch, L, H, G, nc, ngroups, cpg;
-  int Q;
-  float dt_min, dt_max;
-  int dt_softplus, z_bf16, out_bf16, ret_final;
-  int chained;  // grp_state holds entering states (the passing pass ran)
-};
-
-// Workgroup id -> (b, h, chunk group).  Tiles are ordered (b, group, g, head
-// in group); workgroup n runs on XCD n % 8.  Dense calls deal the tiles in
-// contiguous runs to the XCDs, so the heads that share one B/C group run side
-// by side on one XCD and share its L2.  Packed calls, whose rows differ in
-// length, deal units of those heads round-robin over the XCDs instead (unit
-// u on XCD u % 8), so long and short sequences spread over all of them; the
-// grid then has 8 * hpg * ceil(units / 8) workgroups (tile_grid).  With
-// `late_first` the chunk groups are dealt from the last one down (later
-// groups have more to do before their first chunk).
-__device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_here, int64_t &b,
-                                            int64_t &h, int64_t &j, bool late_first = false) {
-  const int64_t total = p.batch * p.H * ngroups_here;
-  const int64_t n = blockIdx.x;
-  const int64_t hpg = p.H / p.G;
-  int64_t T;
-  if (p.cu_seqlens) {
-    const int64_t k = n / 8;
-    T = ((k / hpg) * 8 + n % 8) * hpg + k % hpg;
-  } else {
-    const int64_t per = (total + 7) / 8;
-    T = (n % 8) * per + n / 8;
-  }
-  if (T >= total) return false;
-  const int64_t hh = T % hpg;
-  int64_t rest = T / hpg;
-  const int64_t g = rest % p.G;
-  rest /= p.G;
-  j = rest % ngroups_here;
-  if (late_first) j = ngroups_here - 1 - j;
-  b = rest / ngroups_here;
-  h = g * hpg + hh;
-  return true;
-}
-
-// Tokens of batch row b: [start, start + len) on the token axis.  Dense
-// calls: b*L and L.  Packed calls: the row is sequence b of cu_seqlens,
-// with its offsets clamped to [0, T] (when T is known) and its length to
-// [0, L] (L is then the longest sequence, which the plan is made for), so
-// that malformed offsets never address memory outside x, B, C and out; the
-// main pass reports them through error_flag (offsets_break_contract).
-struct RowSpan {
-  int64_t start, len;
-};
-
-__device__ __forceinline__ RowSpan row_span(const Params &p, int64_t b) {
-  if (!p.cu_seqlens) return {b * p.L, p.L};
-  int64_t s = p.cu_seqlens[b], e = p.cu_seqlens[b + 1];
-  s = s < 0 ? 0 : s;
-  if (p.packed_tokens > 0) {
-    s = s > p.packed_tokens ? p.packed_tokens : s;
-    e = e > p.packed_tokens ? p.packed_tokens : e;
-  }
-  const int64_t len = e - s;
-  return {s, len < 0 ? 0 : (len > p.L ? p.L : len)};
-}
-
-// Whether the offsets of packed row b break the contract of the call: a
-// sequence longer than L, decreasing offsets, a negative offset or one past
-// T (when T is known).
-__device__ __forceinline__ bool offsets_break_contract(const Params &p, int64_t b) {
-  const int64_t s = p.cu_seqlens[b], e = p.cu_seqlens[b + 1];
-  return s < 0 || e < s || e - s > p.L || (p.packed_tokens > 0 && e > p.packed_tokens);
-}
-
-// Chunks of a row and the chunk groups that hold them; an empty row keeps
-// one group, which writes its final state (the initial state).
-__device__ __forceinline__ int64_t row_chunks(const Params &p, int64_t len) {
-  return (len + p.Q - 1) / p.Q;
-}
-__device__ __forceinline__ int64_t row_groups(const Params &p, int64_t len) {
-  const int64_t ng = (row_chunks(p, len) + p.cpg - 1) / p.cpg;
-  return ng < 1 ? 1 : ng;
-}
-
-// Buffer resources and element offsets of one (b, h) sequence.
-template <int N, class IO>
-struct SeqView {
-  rsrc_t x, B, C;
-  uint32_t H, G, h, g;
-  __device__ __forceinline__ SeqView(const Params &p, const RowSpan &rs, int64_t h_, int64_t g_) {
-    const uint64_t L = (uint64_t)rs.len, t0 = (uint64_t)rs.start;
-    H = (uint32_t)p.H;
-    G = (uint32_t)p.G;
-    h = (uint32_t)h_;
-    g = (uint32_t)g_;
-    const uint64_t lhp = L * p.H * kP, lgn = L * p.G * N;
-    const uint64_t ohp = t0 * p.H * kP, ogn = t0 * p.G * N;
-    x = make_rsrc(static_cast<const char *>(p.x) + ohp * IO::esz, (uint32_t)(lhp * IO::esz));
-    B = make_rsrc(static_cast<const char *>(p.B) + ogn * IO::esz, (uint32_t)(lgn * IO::esz));
-    C = make_rsrc(static_cast<const char *>(p.C) + ogn * IO::esz, (uint32_t)(lgn * IO::esz));
-  }
-  __device__ __forceinline__ uint32_t xoff(uint32_t t, uint32_t col) const { return (t * H + h) * kP + col; }
-  __device__ __forceinline__ uint32_t boff(uint32_t t, uint32_t col) const { return (t * G + g) * N + col; }
-};
-
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS
-// operations, then synchronises the workgroup.  Unlike __syncthreads it does
-// not drain outstanding global loads, so prefetched data stays in flight.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Per-chunk scalars in LDS (Lam in log2 units).
-//   lam[j]   inclusive in-chunk prefix of delta*A;  delta[j]
-//   w[j]     exp(Lam_end - Lam_j) delta_j      (chunk_state weights)
-//   u[j]     exp(Lam_m - Lam_j) delta_j, m the reference token (16th) of j's
-//            32-token sub-block; mid[j/32] = Lam_m
-//   dts[j]   raw dt of token j, staged one chunk ahead
-template <int Q> struct ChunkLds {
-  float lam[Q], delta[Q], w[Q], u[Q], dts[Q], mid[Q / 32];
-};
-
-// chunk_cumsum inside the matrix passes.  The raw dt of a chunk is loaded
-// two chunks ahead, one token per thread, and staged in the chunk's LDS
-// scalars one chunk ahead.  Lane l of every wave then takes the tokens
-// l + 64 m of the chunk (m < Q/64) and computes, redundantly in each wave,
-// delta = clamp(softplus(dt + dt_bias)) (0 past the sequence end) and the
-// inclusive in-chunk prefix Lam of delta*A in log2 units (a wavefront scan
-// per 64 tokens plus the running total of the earlier ones).
-// Thread t < Q handles token t; threads past Q load token Q-1 again (one
-// merged request per wave) and store that same value over it, which keeps
-// the load and the LDS store free of branches (a branch here makes the
-// compiler wait for every load in flight).
-__device__ __forceinline__ uint32_t dt_token(int Q) {
-  return threadIdx.x < (uint32_t)Q ? threadIdx.x : (uint32_t)Q - 1;
-}
-
-__device__ __forceinline__ float load_dt(rsrc_t rdt, uint32_t H, uint32_t h, uint32_t t0, int Q) {
-  return __uint_as_float(
-      __builtin_amdgcn_raw_buffer_load_b32(rdt, ((t0 + dt_token(Q)) * H + h) * 4, 0, 0));
-}
-
-template <int Q>
-__device__ __forceinline__ void stage_dt(float v, ChunkLds<Q> &cl) {
-  cl.dts[dt_token(Q)] = v;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves:
-// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row 0's total added
-// to row 1 and row 2's to row 3 (row_bcast:15), then rows 0-1's total to
-// rows 2-3 (row_bcast:31).  Lanes a move does not reach add zero.
-__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
-  int t;
-  const int x = __float_as_int(v);
-  switch (ctrl_sel) {
-    case 0: t = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true); break;  // row_shr:1
-    case 1: t = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true); break;  // row_shr:2
-    case 2: t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true); break;  // row_shr:4
-    case 3: t = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true); break;  // row_shr:8
-    case 4: t = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); break; // row_bcast:15
-    default: t = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); break; // row_bcast:31
-  }
-  return v + __int_as_float(t);
-}
-
-__device__ __forceinline__ float wave_inclusive_sum(float v) {
-#pragma unroll
-  for (int k = 0; k < 6; ++k) v = dpp_add(v, k);
-  return v;
-}
-
-// Discretise and scan the chunk starting at token t0, then fill its LDS
-// scalars (the caller puts a barrier before any reader).  Returns Lam_end and
-// whether |delta*A| <= 7 (log2 units) for every token, which keeps the
-// factored intra-chunk decay of the main pass inside fp32 range.
-template <int Q>
-__device__ __forceinline__ void chunk_prep(const Params &p, uint32_t t0, uint64_t len,
-                                           float a_h, float bias, ChunkLds<Q> &cl, float &lend,
-                                           bool &factored) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float lam[Q / 64], del[Q / 64];
-  float run = 0.f;
-  bool big = false;
-#pragma unroll
-  for (int m = 0; m < Q / 64; ++m) {
-    float u = cl.dts[lane + 64 * m] + bias;
-    // softplus as max(u, 0) + log1p(exp(-|u|)): no cancellation for negative
-    // u (where log(1 + exp(u)) loses the digits of a small step) and no
-    // overflow for large u; the backward uses the same form
-    if (p.dt_softplus) u = fmaxf(u, 0.f) + log1pf(__expf(-fabsf(u)));
-    const float delta = (t0 + lane + 64 * m < len) ? fminf(fmaxf(u, p.dt_min), p.dt_max) : 0.f;
-    const float a = delta * a_h * kLog2e;
-    big |= fabsf(a) > 7.f;
-    const float v = wave_inclusive_sum(a);
-    lam[m] = v + run;
-    del[m] = delta;
-    run += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  }
-  lend = run;
-  factored = __ballot(big) == 0;
-  // wave w < Q/64 writes the records of tokens 64 w .. 64 w + 63
-  if (w < Q / 64) {
-    float lm = 0.f, dl = 0.f;
-#pragma unroll
-    for (int m = 0; m < Q / 64; ++m)
-      if (m == w) {
-        lm = lam[m];
-        dl = del[m];
-      }
-    const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lm), 16));
-    const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lm), 48));
-    const float mid = (lane < 32) ? m0 : m1;
-    const int t = 64 * w + lane;
-    cl.lam[t] = lm;
-    cl.delta[t] = dl;
-    cl.w[t] = fast_exp2(lend - lm) * dl;
-    cl.u[t] = fast_exp2(mid - lm) * dl;
-    if ((lane & 31) == 16) cl.mid[t >> 5] = lm;
-  }
-}
-
-// Raw global data of one 64-token block: B rows [64][N] and x rows [64][P],
-// spread over the workgroup's T threads in units of 4 rows x 4 columns.
-template <int N, class IO, int T>
-struct BlockRaw {
-  static constexpr int NG = N / 4;                  // column groups of B
-  static constexpr int UB = 16 * NG;                // B units
-  static constexpr int UX = 16 * (kP / 4);          // x units
-  static constexpr int KB_ = (UB + T - 1) / T;      // B units per thread
-  static constexpr int KX = (UX + T - 1) / T;       // x units per thread
-  typename IO::raw4 b[KB_][4];
-  typename IO::raw4 x[KX][4];
-};
-
-// Staging unit u -> (token quad rg in 0..15, column quad cg).  Every 64
-// consecutive units cover an 8 x 8 tile of (rg, cg) pairs, so one wave's load
-// of a row reads 8 column quads (a whole 128-byte line of fp32).  Inside each
-// 16-unit group the pairs lie on a diagonal band: both the row-major writes
-// (rows 4rg+e, 8-byte column quads) and the transposed writes (rows 4cg+c,
-// 8-byte token quads) of the group then fall on 16 distinct LDS bank pairs
-// (LDS writes serve 16 lanes of 8 bytes per cycle over 32 banks).
-__device__ __forceinline__ void unit_of(int u, int &rg, int &cg) {
-  const int i = u & 15, d = (u >> 4) & 3, t = u >> 6, q = i >> 2;
-  rg = (i & 1) + 2 * q + 8 * (t & 1);
-  cg = ((i >> 1) & 1) + 2 * ((q + d) & 3) + 8 * (t >> 1);
-}
-
-// Past-the-end element offset: the buffer range check turns a load from it
-// into zeros (no memory access).  Every row buffer is below 2^31 bytes.
-constexpr uint32_t kNoElem = 0x20000000u;
-
-// Issue the loads of the 64-token block starting at token tb.  The loads are
-// unconditional (units past the block's count read kNoElem) so that they stay
-// in flight until the block is stored.
-template <int N, class IO, int T>
-__device__ __forceinline__ void load_block(const SeqView<N, IO> &sv, uint32_t tb,
-                                           BlockRaw<N, IO, T> &r) {
-  using BR = BlockRaw<N, IO, T>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < BR::KB_; ++k) {
-    const int u = tid + T * k;
-    const bool ok = BR::UB % T == 0 || u < BR::UB;
-    int rg, ng;
-    unit_of(u, rg, ng);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      r.b[k][e] = IO::load4(sv.B, ok ? sv.boff(tb + 4 * rg + e, 4 * ng) : kNoElem);
-  }
-#pragma unroll
-  for (int k = 0; k < BR::KX; ++k) {
-    const int u = tid + T * k;
-    const bool ok = BR::UX % T == 0 || u < BR::UX;
-    int rg, pg;
-    unit_of(u, rg, pg);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      r.x[k][e] = IO::load4(sv.x, ok ? sv.xoff(tb + 4 * rg + e, 4 * pg) : kNoElem);
-  }
-}
-
-// Write a loaded block into LDS in the MMA operand type:
-//   sB  [64][N]  B rows            (A operand of B.C^T; only if WANT_B)
-//   sBT [N][64]  (w_j B_j)^T
-//   sXT [P][64]  x^T
-template <int N, bool F32, class IO, int T, bool WANT_B>
-__device__ __forceinline__ void store_block(const BlockRaw<N, IO, T> &r, int jb, const float *sw,
-                                            typename Mma<F32>::T *sB, typename Mma<F32>::T *sBT,
-                                            typename Mma<F32>::T *sXT) {
-  using E = typename Mma<F32>::T;
-  using quad = typename Mma<F32>::quad;
-  using BR = BlockRaw<N, IO, T>;
-  constexpr int LDN = N + 8, LDJ = kJB + 8;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < BR::KB_; ++k) {
-    const int u = tid + T * k;
-    if (u < BR::UB) {
-      int rg, ng;
-      unit_of(u, rg, ng);
-      const int r0 = 4 * rg;
-      const f32x4 wgt = *reinterpret_cast<const f32x4 *>(&sw[kJB * jb + r0]);
-      f32x4 v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = IO::cvt4(r.b[k][e]);
-        if (WANT_B) {
-          quad q;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) q[c] = (E)v[e][c];
-          *reinterpret_cast<quad *>(&sB[(r0 + e) * LDN + 4 * ng]) = q;
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        quad q;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] = (E)(wgt[e] * v[e][c]);
-        *reinterpret_cast<quad *>(&sBT[(4 * ng + c) * LDJ + r0]) = q;
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < BR::KX; ++k) {
-    const int u = tid + T * k;
-    if (u < BR::UX) {
-      int rg, pg;
-      unit_of(u, rg, pg);
-      const int r0 = 4 * rg;
-      f32x4 v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = IO::cvt4(r.x[k][e]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        quad q;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] = (E)v[e][c];
-        *reinterpret_cast<quad *>(&sXT[(4 * pg + c) * LDJ + r0]) = q;
-      }
-    }
-  }
-}
-
-// The z gate of one 64-token block, staged like x so each row's epilogue
-// finds it in LDS: unit u holds row u/8, columns 8 (u%8) .. +8.
-typedef unsigned int u32x4v __attribute__((vector_size(16)));
-template <int T>
-struct ZRaw {
-  static constexpr int K = 512 / T;
-  u32x4v lo[K], hi[K];  // 8 fp32, or 8 bf16 in lo
-};
-
-template <int T>
-__device__ __forceinline__ void load_z(rsrc_t rz, bool bf16, uint32_t H, uint32_t h, uint32_t tb,
-                                       ZRaw<T> &r) {
-#pragma unroll
-  for (int k = 0; k < ZRaw<T>::K; ++k) {
-    const int u = threadIdx.x + T * k;
-    const uint32_t off = ((tb + u / 8) * H + h) * kP + 8 * (u % 8);
-    if (bf16) {
-      r.lo[k] = IoBF16::load8(rz, off);
-    } else {
-      r.lo[k] = __builtin_amdgcn_raw_buffer_load_b128(rz, off * 4, 0, 0);
-      r.hi[k] = __builtin_amdgcn_raw_buffer_load_b128(rz, off * 4 + 16, 0, 0);
-    }
-  }
-}
-
-template <int T>
-__device__ __forceinline__ void store_z(const ZRaw<T> &r, bool bf16, float *sZ) {
-  constexpr int LDZ = kP + 4;
-#pragma unroll
-  for (int k = 0; k < ZRaw<T>::K; ++k) {
-    const int u = threadIdx.x + T * k;
-    f32x4 lo, hi;
-    if (bf16) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo[e] = IoBF16::cvt8(r.lo[k], e);
-        hi[e] = IoBF16::cvt8(r.lo[k], 4 + e);
-      }
-    } else {
-      lo = __builtin_bit_cast(f32x4, r.lo[k]);
-      hi = __builtin_bit_cast(f32x4, r.hi[k]);
-    }
-    // lanes 4..7 of each group of 8 write their halves in the other order,
-    // so each 16-byte write instruction covers all 32 banks once
-    float *dst = &sZ[(u / 8) * LDZ + 8 * (u % 8)];
-    const bool sw = (u & 4) != 0;
-    *reinterpret_cast<f32x4 *>(dst + (sw ? 4 : 0)) = sw ? hi : lo;
-    *reinterpret_cast<f32x4 *>(dst + (sw ? 0 : 4)) = sw ? lo : hi;
-  }
-}
-
-// Ownership of the P x N state by the W waves: wave w holds rows p in
-// [16 (w%4), +16) and NN = N/(4W/4... ) consecutive 16-column tiles starting
-// at tile (w/4) NN, in MFMA accumulator layout.
-template <int N, int W>
-struct StateSplit {
-  static constexpr int NN = (N / 16) / (W / 4);  // n-tiles per wave
-  static __device__ __forceinline__ int row(int r) {
-    return 16 * ((threadIdx.x >> 6) & 3) + 4 * ((threadIdx.x & 63) >> 4) + r;
-  }
-  static __device__ __forceinline__ int col(int t) {
-    return 16 * ((threadIdx.x >> 8) * NN + t) + (threadIdx.x & 15);
-  }
-};
-
-// Main-pass waves per workgroup for a chunk size.
-template <int Q> constexpr int main_waves() { return Q == 256 ? 8 : 4; }
-
-// Group records in the workspace (aggregates, entering states) are kept in
-// the main pass's register order: slice t (of NN) of main-pass thread i, the
-// four rows row(0..3) of column col(t), sits at float (t * T + i) * 4 (T
-// main-pass threads), so each slice of a record is one coalesced 16-byte
-// load per lane.  rec_index maps the element (row p, column n) of the P x N
-// state to its position; rec_element is the inverse.
-template <int N, int WM>
-__device__ __forceinline__ uint32_t rec_index(int row, int col) {
-  constexpr int NN = StateSplit<N, WM>::NN, T = 64 * WM;
-  const int tile = col >> 4;
-  const int w = 4 * (tile / NN) + (row >> 4);
-  const int tid = 64 * w + 16 * ((row & 15) >> 2) + (col & 15);
-  return (uint32_t)(((tile % NN) * T + tid) * 4 + (row & 3));
-}
-
-template <int N, int WM>
-__device__ __forceinline__ void rec_element(uint32_t e, int &row, int &col) {
-  constexpr int NN = StateSplit<N, WM>::NN, T = 64 * WM;
-  const int r = (int)(e & 3), t = (int)((e >> 2) / T), tid = (int)((e >> 2) % T);
-  const int w = tid >> 6, lane = tid & 63;
-  row = 16 * (w & 3) + 4 * (lane >> 4) + r;
-  col = 16 * ((w >> 2) * NN + t) + (lane & 15);
-}
-
-// chunk_state on one staged block: S += X^T diag(w) B over the block's 64
-// tokens, for this wave's share of the state.
-template <int N, bool F32, int W>
-__device__ __forceinline__ void state_block_mma(const typename Mma<F32>::T *sXT,
-                                                const typename Mma<F32>::T *sBT, f32x4 *sacc) {
-  using frag = typename Mma<F32>::frag;
-  constexpr int LDJ = kJB + 8;
-  constexpr int NN = StateSplit<N, W>::NN;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lq = lane >> 4;
-  const int ps = w & 3, n0 = (w >> 2) * NN;
-#pragma unroll 1
-  for (int kb = 0; kb < kJB / 32; ++kb) {
-    const frag a = *reinterpret_cast<const frag *>(&sXT[(16 * ps + lr) * LDJ + 32 * kb + 8 * lq]);
-#pragma unroll
-    for (int t = 0; t < NN; ++t) {
-      const frag bf =
-          *reinterpret_cast<const frag *>(&sBT[(16 * (n0 + t) + lr) * LDJ + 32 * kb + 8 * lq]);
-      sacc[t] = mma(a, bf, sacc[t]);
-    }
-  }
-}
-
-// Work split of a chunk's Q output rows (NT = Q/16 row tiles) over W waves.
-// Row tiles are dealt in mirrored sets (s, 7-s, 8+s, 15-s, ...) so the
-// causal work per SIMD is even; with fewer tiles than waves the waves
-// sharing a SIMD split the head dim instead.
-template <int Q, int W>
-struct RowSplit {
-  static constexpr int NT = Q / 16;
-  static constexpr int NR = NT >= W ? NT / W : 1;   // row tiles per wave
-  static constexpr int PT = NT >= W ? 4 : 4 * NT / W;  // p-tiles per wave
-  static __device__ __forceinline__ int tile(int k, int w) {
-    if (NT < W) return w % NT;                // NT = 4, W = 8
-    if (W == 4) {                             // tiles w, 7-w, 8+w, 15-w
-      const int pi = k >> 1;
-      return (k & 1) ? 8 * pi + 7 - w : 8 * pi + w;
-    }
-    // W = 8: SIMD s = w%4 owns tiles s, 7-s (NT = 8) or s, 7-s, 8+s, 15-s
-    // (NT = 16), shared by its two waves
-    const int s = w & 3, hf = w >> 2;
-    if (NT == 8) return hf ? 7 - s : s;
-    return hf ? (k ? 8 + s : 7 - s) : (k ? 15 - s : s);
-  }
-  static __device__ __forceinline__ int pt0(int w) { return NT < W ? PT * (w / NT) : 0; }
-};
-
-__device__ __forceinline__ int nblocks(int Qc) { return (Qc + kJB - 1) / kJB; }
-
-// ---------------------------------------------------------------- kernels
-
-// First pass (only when a sequence is split into several chunk groups): the
-// state each of the first ngroups-1 groups builds from a zero start (its
-// aggregate), and the group's total decay.  Four waves walk the group's 64-token blocks (all its
-// chunks are full) with two blocks of B and x in flight: a block's buffer is
-// refilled with the block two ahead as soon as it is staged in LDS.
-template <int Q, int N, bool F32, class IO>
-__global__ __launch_bounds__(256) void ssd_group_state_kernel(Params p) {
-  constexpr int W = 4, T = 64 * W, NB = Q / kJB;
-  using E = typename Mma<F32>::T;
-  using SS = StateSplit<N, W>;
-  constexpr int LDJ = kJB + 8;
-  constexpr int NN = SS::NN;
-  __shared__ __attribute__((aligned(16))) E sBT[N * LDJ];
-  __shared__ __attribute__((aligned(16))) E sXT[kP * LDJ];
-  __shared__ __attribute__((aligned(16))) ChunkLds<Q> clb[2];
-
-  int64_t b, h, j;
-  if (!decode_tile(p, p.ngroups - 1, b, h, j)) return;
-  const RowSpan rs = row_span(p, b);
-  if (j >= row_groups(p, rs.len) - 1) return;  // the row's last group, or past its end
-  const int64_t g = h / (p.H / p.G);
-  const int64_t bh = b * p.H + h;
-  const SeqView<N, IO> sv(p, rs, h, g);
-
-  f32x4 sacc[NN];
-#pragma unroll
-  for (int t = 0; t < NN; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float lgrp = 0.f, lend2 = 0.f;
-  const int64_t c_begin = j * p.cpg, c_end = c_begin + p.cpg;  // never the last group
-  const int nblk = (int)p.cpg * NB;
-  const uint32_t tg = (uint32_t)(c_begin * Q);
-  auto tok = [&](int i) { return tg + (uint32_t)(kJB * (i < nblk ? i : nblk - 1)); };
-
-  const rsrc_t rdt = make_rsrc(p.dt + rs.start * p.H, (uint32_t)(rs.len * p.H * 4));
-  const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
-  // Each block buffer also carries the raw dt of the block one chunk later
-  // (token 64 k + t of the group for block k + NB, thread t < 64; later
-  // threads repeat token 63); it is staged in the next chunk's LDS scalars
-  // when the block is staged, so its wait is the block's own.  The first
-  // chunk's dt is staged up front.
-  auto load_bdt = [&](int k) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-        rdt, ((tg + (uint32_t)(kJB * k) + dt_token(kJB)) * sv.H + sv.h) * 4, 0, 0));
-  };
-  stage_dt<Q>(load_dt(rdt, sv.H, sv.h, tg, Q), clb[c_begin & 1]);
-  // (scheduling barriers keep every buffer's loads in the same issue order
-  // before and inside the loop, so the compiler can count them exactly)
-  BlockRaw<N, IO, T> nx0, nx1;
-  load_block<N, IO, T>(sv, tok(0), nx0);
-  float bdt0 = load_bdt(NB);
-  __builtin_amdgcn_sched_barrier(0);
-  load_block<N, IO, T>(sv, tok(1), nx1);
-  float bdt1 = load_bdt(1 + NB);
-  __builtin_amdgcn_sched_barrier(0);
-  lds_barrier();
-
-  auto step = [&](BlockRaw<N, IO, T> &buf, float &bdt, int i) {
-    const int jb = i % NB;
-    const int64_t c = c_begin + i / NB;
-    ChunkLds<Q> &cl = clb[c & 1];
-    if (jb == 0) {
-      bool factored;
-      chunk_prep<Q>(p, (uint32_t)(c * Q), (uint64_t)rs.len, a_h, bias, cl, lend2, factored);
-      const float dec = fast_exp2(lend2);
-#pragma unroll
-      for (int t = 0; t < NN; ++t) sacc[t] *= dec;
-      lgrp += lend2;
-    }
-    lds_barrier();
-    store_block<N, F32, IO, T, false>(buf, jb, cl.w, nullptr, sBT, sXT);
-    // dt of the same block position in chunk c+1, into the other buffer
-    // (its readers from chunk c-1 passed the barrier above)
-    clb[(c + 1) & 1].dts[kJB * jb + dt_token(kJB)] = bdt;
-    lds_barrier();
-    load_block<N, IO, T>(sv, tok(i + 2), buf);  // past the group's end: its last block, unused
-    bdt = load_bdt(i + 2 + NB);
-    __builtin_amdgcn_sched_barrier(0);
-    state_block_mma<N, F32, W>(sXT, sBT, sacc);
-  };
-  int i = 0;
-  for (; i + 1 < nblk; i += 2) {
-    step(nx0, bdt0, i);
-    step(nx1, bdt1, i + 1);
-  }
-  if (i < nblk) step(nx0, bdt0, i);
-  // the aggregate, in the main pass's register order
-  const int64_t slot = bh * (p.ngroups - 1) + j;
-  float *dst = p.grp_state + slot * (int64_t)(kP * N);
-  constexpr int WM = main_waves<Q>();
-  if (WM == W) {
-#pragma unroll
-    for (int t = 0; t < NN; ++t)
-      *reinterpret_cast<f32x4 *>(dst + (t * T + threadIdx.x) * 4) = sacc[t];
-  } else {
-#pragma unroll
-    for (int t = 0; t < NN; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[rec_index<N, WM>(SS::row(r), SS::col(t))] = sacc[t][r];
-  }
-  if (threadIdx.x == 0) p.grp_lam[slot] = lgrp;
-}
-
-// state_passing across chunk groups as its own pass (used when sequences
-// have more than kFoldGroups+1 groups; elementwise over P*N, sequential over
-// groups): S = exp(Lam_grp) S + S_grp; slot j is overwritten with the state
-// entering group j+1.
-template <int N, int WM>
-__global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p) {
-  constexpr int PN = kP * N;
-  constexpr int64_t blocks_per_bh = PN / 256;
-  const int64_t bh = blockIdx.x / blocks_per_bh;
-  const int64_t e = (blockIdx.x % blocks_per_bh) * 256 + threadIdx.x;  // record order
-  float S = 0.f;
-  if (p.h0) {
-    int row, col;
-    rec_element<N, WM>((uint32_t)e, row, col);
-    S = p.h0[bh * PN + row * N + col];
-  }
-  const int64_t ng1 = p.ngroups - 1;
-  const int64_t ng1_row = row_groups(p, row_span(p, bh / p.H).len) - 1;  // filled slots
-  for (int64_t jj = 0; jj < ng1_row; ++jj) {
-    const int64_t slot = bh * ng1 + jj;
-    S = fast_exp2(p.grp_lam[slot]) * S + p.grp_state[slot * PN + e];
-    p.grp_state[slot * PN + e] = S;
-  }
-}
-
-// Main pass: chunk_scan over the chunks of one group with W waves, carrying
-// the state.  Per chunk: the inter-chunk term C.S_in^T from the carried
-// state, then per 64-token block the intra-chunk term, the block's
-// contribution to the carried state and the epilogue of the rows the block
-// completes; the next block's loads are issued before its matrix work.
-template <int Q, int N, bool F32, class IO, int W, bool HAS_Z>
-__global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
-  constexpr int T = 64 * W;
-  using E = typename Mma<F32>::T;
-  using frag = typename Mma<F32>::frag;
-  using quad = typename Mma<F32>::quad;
-  using RS = RowSplit<Q, W>;
-  using SS = StateSplit<N, W>;
-  constexpr int NR = RS::NR, PT = RS::PT;
-  constexpr int KB = N / 32;  // K blocks over the state dim
-  constexpr int NN = SS::NN;
-  constexpr int LDN = N + 8, LDJ = kJB + 8, LDZ = kP + 4;
-  // hoist the fp16 M.X operand fragments out of the row-tile loop only when
-  // the state and output accumulators take fewer than 64 registers (with 64,
-  // as for 128-token chunks of a 128-wide state, the hoisted fragments spill;
-  // the fp32 check path keeps them unhoisted too)
-  constexpr bool kHoistX = !F32 && 4 * NN + 4 * NR * PT < 64;
-  __shared__ __attribute__((aligned(16))) E sB[kJB * LDN];
-  __shared__ __attribute__((aligned(16))) E sBT[N * LDJ];
-  __shared__ __attribute__((aligned(16))) E sXT[kP * LDJ];
-  __shared__ __attribute__((aligned(16))) E sS[kP * LDN];
-  __shared__ __attribute__((aligned(16))) float sZ[HAS_Z ? kJB * LDZ : 4];
-  __shared__ __attribute__((aligned(16))) ChunkLds<Q> clb[2];
-
-  int64_t b, h, j;
-  if (!decode_tile(p, p.ngroups, b, h, j, true)) return;
-  if (p.cu_seqlens && p.error_flag && j == 0 && threadIdx.x == 0 && offsets_break_contract(p, b))
-    __builtin_amdgcn_raw_buffer_store_b32(1u, make_rsrc(p.error_flag, 4u), 0, 0, 0);
-  const RowSpan rs = row_span(p, b);
-  const int64_t ng_row = row_groups(p, rs.len), nc_row = row_chunks(p, rs.len);
-  if (j >= ng_row) return;  // past the end of a shorter packed sequence
-  // the wave index is uniform: read it into a scalar so per-wave tests branch
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lr = lane & 15, lq = lane >> 4;
-  const int pt0 = RS::pt0(w);
-  const int64_t g = h / (p.H / p.G);
-  const SeqView<N, IO> sv(p, rs, h, g);
-  const uint64_t lhp = (uint64_t)rs.len * p.H * kP, ohp = (uint64_t)rs.start * p.H * kP;
-  const int osz = p.out_bf16 ? 2 : 4, zsz = p.z_bf16 ? 2 : 4;
-  const rsrc_t rout = make_rsrc(static_cast<char *>(p.out) + ohp * osz, (uint32_t)(lhp * osz));
-  const rsrc_t rz = make_rsrc(HAS_Z ? static_cast<const char *>(p.z) + ohp * zsz : nullptr,
-                              HAS_Z ? (uint32_t)(lhp * zsz) : 0u);
-  const bool z_bf16 = p.z_bf16 != 0;
-  const float Dh = p.D ? p.D[h] : 0.f;
-  const int64_t bh = b * p.H + h;
-  const int64_t c_begin = j * p.cpg;
-  const int64_t c_end = (c_begin + p.cpg < nc_row) ? c_begin + p.cpg : nc_row;
-  auto qc_of = [&](int64_t c) { return (int)((rs.len - c * Q) < Q ? (rs.len - c * Q) : Q); };
-
-  // prefetch registers: next 64-token block (and its z), next chunk's C rows
-  // and records
-  BlockRaw<N, IO, T> nxt;
-  ZRaw<T> nz;
-  auto load_zb = [&](uint32_t tb) {
-    if (HAS_Z) load_z<T>(rz, z_bf16, sv.H, sv.h, tb, nz);
-  };
-  const rsrc_t rdt = make_rsrc(p.dt + rs.start * p.H, (uint32_t)(rs.len * p.H * 4));
-  const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
-  typename IO::raw8 craw[NR][KB];
-  auto load_c = [&](uint32_t t0) {
-#pragma unroll
-    for (int k = 0; k < NR; ++k)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        craw[k][kb] = IO::load8(sv.C, sv.boff(t0 + 16 * RS::tile(k, w) + lr, 32 * kb + 8 * lq));
-  };
-  // C rows are prefetched during the previous chunk's last block when they
-  // fit in 16 registers, else loaded at the start of their chunk
-  constexpr bool kPrefetchC = NR * KB * sizeof(typename IO::raw8) <= 64;
-
-  // Prologue.  Loads retire in issue order: the first two chunks' dt are
-  // asked for first, so staging dt does not wait for the first block; the
-  // block (its z, the first chunk's prefetched C rows) follows, then the
-  // initial state and the first R group aggregates, which arrive with the
-  // block instead of one round trip after it.
-  // dt two chunks ahead in registers, one chunk ahead in LDS.
-  const float dt0 = load_dt(rdt, sv.H, sv.h, (uint32_t)(c_begin * Q), Q);
-  float dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c_begin + 1 < c_end ? c_begin + 1 : c_begin) * Q), Q);
-
-  // state entering this group: state_passing over the groups before it,
-  // S = exp(Lam_grp[i]) S + S_grp[i] for i < j starting from h0 (or zero),
-  // elementwise in this thread's share of the state; the aggregates are
-  // loaded R at a time through a range holding slots i_begin..j-1 (a missing
-  // h0, and slots past j-1, read as zeros through the range check).  When the
-  // passing pass already chained the groups, slot j-1 holds the entering
-  // state: the same loop then runs once, from zero.
-  f32x4 sacc[NN];
-  {
-    const bool from_zero = p.chained && j > 0;
-    const int64_t i_begin = from_zero ? j - 1 : 0;
-    const float *h0 = (p.h0 && !from_zero) ? p.h0 + bh * (int64_t)(kP * N) : nullptr;
-    const rsrc_t ri = make_rsrc(h0, h0 ? (uint32_t)(kP * N * 4) : 0u);
-    constexpr int R = 16 / NN > 0 ? 16 / NN : 1;
-    const int64_t ng1 = p.ngroups - 1;
-    // at most kFoldGroups + 1 slots (one when chained): far below 2^32 bytes
-    const rsrc_t ra = make_rsrc(j > i_begin ? p.grp_state + (bh * ng1 + i_begin) * (int64_t)(kP * N)
-                                            : nullptr,
-                                (uint32_t)((j - i_begin) * (kP * N * 4)));
-    const float *glam = p.grp_lam + bh * ng1;
-    load_block<N, IO, T>(sv, (uint32_t)(c_begin * Q), nxt);
-    load_zb((uint32_t)(c_begin * Q));
-    if (kPrefetchC) load_c((uint32_t)(c_begin * Q));
-    f32x4 v[R][NN];
-    auto load_aggs = [&](int64_t i0) {
-#pragma unroll
-      for (int q = 0; q < R; ++q)
-#pragma unroll
-        for (int t = 0; t < NN; ++t)
-          v[q][t] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                         ra, (uint32_t)(((i0 - i_begin + q) * (kP * N) + (t * T + threadIdx.x) * 4) * 4),
-                         0, 0));
-    };
-#pragma unroll
-    for (int t = 0; t < NN; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sacc[t][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            ri, (uint32_t)(SS::row(r) * N + SS::col(t)) * 4, 0, 0));
-    load_aggs(i_begin);
-    stage_dt<Q>(dt0, clb[c_begin & 1]);
-    for (int64_t i0 = i_begin; i0 < j; i0 += R) {
-      if (i0 != i_begin) load_aggs(i0);
-#pragma unroll
-      for (int q = 0; q < R; ++q) {
-        if (i0 + q >= j) break;
-        const float dec = fast_exp2(glam[i0 + q]);
-#pragma unroll
-        for (int t = 0; t < NN; ++t) sacc[t] = dec * sacc[t] + v[q][t];
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < NN; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sS[SS::row(r) * LDN + SS::col(t)] = (E)sacc[t][r];
-  }
-  lds_barrier();  // the first chunk's staged dt
-
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    const uint32_t t0 = (uint32_t)(c * Q);
-    const int Qc = qc_of(c);
-    ChunkLds<Q> &cl = clb[c & 1];
-    if (!kPrefetchC) load_c(t0);
-    float lend2;
-    bool factored;
-    chunk_prep<Q>(p, t0, (uint64_t)rs.len, a_h, bias, cl, lend2, factored);
-    lds_barrier();
-    // chunk c-1's readers of the other buffer passed the barrier above
-    stage_dt<Q>(dtr, clb[(c + 1) & 1]);
-    dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c + 2 < c_end ? c + 2 : c) * Q), Q);
-
-    // B operand of B.C^T and A operand of C.S^T share this layout
-    frag cfr[NR][KB];
-#pragma unroll
-    for (int k = 0; k < NR; ++k)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) cfr[k][kb][s] = (E)IO::cvt8(craw[k][kb], s);
-
-    // inter-chunk term: Y = diag(exp(Lam)) C S_in^T
-    f32x4 yacc[NR][PT];
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const int row0 = 16 * RS::tile(k, w);
-      const f32x4 lam4 = *reinterpret_cast<const f32x4 *>(&cl.lam[row0 + 4 * lq]);
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const frag sf =
-              *reinterpret_cast<const frag *>(&sS[(16 * (pt0 + pt) + lr) * LDN + 32 * kb + 8 * lq]);
-          acc = mma(cfr[k][kb], sf, acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= fast_exp2(lam4[r]);
-        yacc[k][pt] = acc;
-      }
-    }
-
-    // carried state: S <- exp(Lam_end) S, then += this chunk's S_loc below
-    {
-      const float dec = fast_exp2(lend2);
-#pragma unroll
-      for (int t = 0; t < NN; ++t) sacc[t] *= dec;
-    }
-
-    const int nb = nblocks(Qc);
-    for (int jb = 0; jb < nb; ++jb) {
-      lds_barrier();
-      store_block<N, F32, IO, T, true>(nxt, jb, cl.w, sB, sBT, sXT);
-      if (HAS_Z) store_z<T>(nz, z_bf16, sZ);
-      lds_barrier();
-      {
-        // next block: the chunk's next one, else the next chunk's first, else
-        // (last block of the group) this one again, unused
-        const bool last = jb + 1 == nb;
-        const uint32_t tn = !last ? t0 + kJB * (jb + 1) : (c + 1 < c_end) ? t0 + Q : t0 + kJB * jb;
-        load_block<N, IO, T>(sv, tn, nxt);
-        load_zb(tn);
-        if (kPrefetchC && last) load_c((c + 1 < c_end) ? t0 + Q : t0);
-      }
-      // intra-chunk term for this wave's row tiles against tokens of block jb,
-      // one 32-token sub-block at a time (its B fragments serve every row
-      // tile of the wave that reaches it)
-#pragma unroll 1
-      for (int js = 0; js < kJB / 32; ++js) {
-        const int jbase = kJB * jb + 32 * js;
-        bool any = false;
-#pragma unroll
-        for (int k = 0; k < NR; ++k) any |= jbase <= 16 * RS::tile(k, w) + 15;
-        if (!any) continue;
-        frag a0[KB], a1[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          a0[kb] = *reinterpret_cast<const frag *>(&sB[(32 * js + lr) * LDN + 32 * kb + 8 * lq]);
-          a1[kb] = *reinterpret_cast<const frag *>(&sB[(32 * js + 16 + lr) * LDN + 32 * kb + 8 * lq]);
-        }
-        // x^T fragments of the sub-block (B operand of M.X; K slots j =
-        // 32 js + 4 lq + s and + 16).  When the accumulators leave room they
-        // are read once for all of the wave's row tiles, ahead of the B.C^T
-        // products; otherwise each row tile reads them as it needs them.
-        auto x_frag = [&](int pt) {
-          const E *xrow = &sXT[(16 * (pt0 + pt) + lr) * LDJ + 32 * js + 4 * lq];
-          const quad lo = *reinterpret_cast<const quad *>(xrow);
-          const quad hi = *reinterpret_cast<const quad *>(xrow + 16);
-          frag f;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            f[s] = lo[s];
-            f[4 + s] = hi[s];
-          }
-          return f;
-        };
-        frag xb[kHoistX ? PT : 1];
-        if constexpr (kHoistX) {
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt) xb[pt] = x_frag(pt);
-        }
-        const int ja0 = jbase + 4 * lq;
-        const float lmid = cl.mid[jbase >> 5];
-#pragma unroll
-        for (int k = 0; k < NR; ++k) {
-          const int row0 = 16 * RS::tile(k, w);
-          if (jbase > row0 + 15) continue;
-          const int i = row0 + lr;
-          const float li = cl.lam[i];
-          // G^T[j][i] = B_j . C_i for j in [jbase, jbase+32), two 16x16 tiles
-          f32x4 g0 = f32x4{0.f, 0.f, 0.f, 0.f}, g1 = g0;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            g0 = mma(a0[kb], cfr[k][kb], g0);
-            g1 = mma(a1[kb], cfr[k][kb], g1);
-          }
-          // M[i][j] = G[i][j] exp(Lam_i - Lam_j) delta_j (j <= i), held as the
-          // A operand of M.X: lane keeps row i, K slots j = jbase+4lq+r and
-          // jbase+16+4lq+r.  The decay factors as exp(Lam_i - Lam_m) times
-          // exp(Lam_m - Lam_j) delta_j with m the sub-block's reference token.
-          float ma[4], mc[4];
-          if (factored) {
-            const float vi = fast_exp2(li - lmid);
-            const f32x4 ua = *reinterpret_cast<const f32x4 *>(&cl.u[ja0]);
-            const f32x4 uc = *reinterpret_cast<const f32x4 *>(&cl.u[ja0 + 16]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              ma[r] = g0[r] * ua[r] * vi;
-              mc[r] = g1[r] * uc[r] * vi;
-            }
-          } else {
-            const f32x4 la = *reinterpret_cast<const f32x4 *>(&cl.lam[ja0]);
-            const f32x4 lc = *reinterpret_cast<const f32x4 *>(&cl.lam[ja0 + 16]);
-            const f32x4 da = *reinterpret_cast<const f32x4 *>(&cl.delta[ja0]);
-            const f32x4 dc = *reinterpret_cast<const f32x4 *>(&cl.delta[ja0 + 16]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              ma[r] = g0[r] * (fast_exp2(li - la[r]) * da[r]);
-              mc[r] = g1[r] * (fast_exp2(li - lc[r]) * dc[r]);
-            }
-          }
-          frag mf;
-          if (jbase + 31 > row0) {  // the sub-block meets the diagonal: mask j > i
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              mf[r] = (E)(ja0 + r <= i ? ma[r] : 0.f);
-              mf[4 + r] = (E)(ja0 + 16 + r <= i ? mc[r] : 0.f);
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              mf[r] = (E)ma[r];
-              mf[4 + r] = (E)mc[r];
-            }
-          }
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt) {
-            if constexpr (kHoistX) yacc[k][pt] = mma(mf, xb[pt], yacc[k][pt]);
-            else yacc[k][pt] = mma(mf, x_frag(pt), yacc[k][pt]);
-          }
-        }
-      }
-
-      // chunk_state contribution of this block to the carried state
-      state_block_mma<N, F32, W>(sXT, sBT, sacc);
-
-      // epilogue of the row tiles that lie in this block (their sums are
-      // complete): + D x with x from the staged block, the z gate from the
-      // staged z, store (rows past the sequence end are dropped by the buffer
-      // range check)
-#pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        const int row0 = 16 * RS::tile(k, w);
-        if ((row0 >> 6) != jb) continue;
-        const int lrow = row0 - kJB * jb + 4 * lq;  // row within the block, + r
-        f32x4 yv[PT];
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          const int col = 16 * (pt0 + pt) + lr;
-          const quad xq = *reinterpret_cast<const quad *>(&sXT[col * LDJ + lrow]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float y = yacc[k][pt][r] + Dh * (float)xq[r];
-            if (HAS_Z) {
-              const float zz = sZ[(lrow + r) * LDZ + col];
-              y *= zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz));
-            }
-            yv[pt][r] = y;
-          }
-        }
-        const uint32_t off0 = sv.xoff(t0 + kJB * jb + lrow, 16 * pt0 + lr);
-        const uint32_t rstep = sv.H * kP;  // elements between consecutive tokens
-        if (p.out_bf16) {
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(yv[pt][r]), rout,
-                                                    (off0 + r * rstep + 16 * pt) * 2, 0, 0);
-        } else {
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[pt][r]), rout,
-                                                    (off0 + r * rstep + 16 * pt) * 4, 0, 0);
-        }
-      }
-    }
-
-    // the state entering the next chunk, as the C.S^T operand (all waves
-    // finished reading sS before the block loop's barriers)
-#pragma unroll
-    for (int t = 0; t < NN; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sS[SS::row(r) * LDN + SS::col(t)] = (E)sacc[t][r];
-  }
-
-  if (p.ret_final && j == ng_row - 1) {
-    float *dst = p.final_state + bh * (int64_t)(kP * N);
-#pragma unroll
-    for (int t = 0; t < NN; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[SS::row(r) * N + SS::col(t)] = sacc[t][r];
-  }
-}
+namespace ssd_fwd_impl {
 
 // ---------------------------------------------------------------- host side
 
@@ -1162,19 +13,6 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool is_supported_chunk(int64_t q) { return q == 64 || q == 128 || q == 256; }
-
-// The main pass chains up to this many group aggregates itself; with more
-// groups a separate passing pass chains them once (measured: 8 aggregates
-// per workgroup cost less than the extra pass, 15 cost more).
-constexpr int64_t kFoldGroups = 8;
-
-// Workspace (only when a sequence is cut into several chunk groups): the
-// group states and group decays.
-struct Plan {
-  int64_t nc, cpg, ngroups;
-  size_t state_bytes, lam_bytes;
-  size_t total() const { return state_bytes + lam_bytes; }
-};
 
 // Validation of everything but pointers.
 ssd_status check_shape(const ssd_desc *d, int64_t chunk) {
@@ -1185,14 +23,18 @@ ssd_status check_shape(const ssd_desc *d, int64_t chunk) {
   if (d->nheads % d->ngroups != 0) return SSD_ERR_INVALID_ARG;
   if (d->x_dtype != SSD_F32 && d->x_dtype != SSD_BF16 && d->x_dtype != SSD_F16)
     return SSD_ERR_INVALID_ARG;
+  if (d->bc_dtype != SSD_F32 && d->bc_dtype != SSD_BF16 && d->bc_dtype != SSD_F16)
+    return SSD_ERR_INVALID_ARG;
   if (d->z_dtype != SSD_F32 && d->z_dtype != SSD_BF16 && d->z_dtype != SSD_F16)
     return SSD_ERR_INVALID_ARG;
   if (d->out_dtype != SSD_F32 && d->out_dtype != SSD_BF16 && d->out_dtype != SSD_F16)
     return SSD_ERR_INVALID_ARG;
-  if (d->mma != SSD_MMA_F16 && d->mma != SSD_MMA_F32) return SSD_ERR_INVALID_ARG;
-  if (d->chunks_per_wg < 0 || d->reserved != 0 || d->packed_tokens < 0) return SSD_ERR_INVALID_ARG;
+  if (d->mma != SSD_MMA_F16 && d->mma != SSD_MMA_BF16 && d->mma != SSD_MMA_F32)
+    return SSD_ERR_INVALID_ARG;
+  if (d->chunks_per_wg < 0 || d->packed_tokens < 0) return SSD_ERR_INVALID_ARG;
   if (!(d->dt_min <= d->dt_max)) return SSD_ERR_INVALID_ARG;  // also rejects NaN
-  if (d->x_dtype == SSD_F16 || d->z_dtype == SSD_F16 || d->out_dtype == SSD_F16)
+  if (d->x_dtype == SSD_F16 || d->bc_dtype == SSD_F16 || d->z_dtype == SSD_F16 ||
+      d->out_dtype == SSD_F16)
     return SSD_ERR_UNSUPPORTED;
   if (d->headdim != kP) return SSD_ERR_UNSUPPORTED;
   if (d->dstate != 64 && d->dstate != 128) return SSD_ERR_UNSUPPORTED;
@@ -1247,67 +89,6 @@ Plan make_plan(const ssd_desc *d, int64_t chunk) {
 }
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
-
-
-// Workgroups covering `ngroups_here` chunk groups of every (b, h), as
-// decode_tile deals them.
-int64_t tile_grid(const Params &p, int64_t ngroups_here) {
-  const int64_t hpg = p.H / p.G;
-  if (p.cu_seqlens) {
-    const int64_t units = p.batch * p.G * ngroups_here;
-    return 8 * hpg * ((units + 7) / 8);
-  }
-  return 8 * ((p.batch * p.H * ngroups_here + 7) / 8);
-}
-
-template <int Q, int N, bool F32, class IO>
-ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, const ssd_desc *d) {
-  const int64_t bh = prm.batch * prm.H;
-  const int64_t g2 = tile_grid(prm, pl.ngroups);  // the largest grid, checked before any launch
-  if (g2 > (int64_t)UINT32_MAX) return SSD_ERR_UNSUPPORTED;
-  if (pl.ngroups > 1) {
-    const int64_t g1 = tile_grid(prm, pl.ngroups - 1);
-    hipLaunchKernelGGL((ssd_group_state_kernel<Q, N, F32, IO>), dim3((unsigned)g1), dim3(256),
-                       0, stream, prm);
-    if (prm.chained)
-      hipLaunchKernelGGL((ssd_group_passing_kernel<N, main_waves<Q>()>),
-                         dim3((unsigned)(bh * (kP * N / 256))), dim3(256), 0, stream, prm);
-  }
-  if (d->ev_main_begin && hipEventRecord(static_cast<hipEvent_t>(d->ev_main_begin), stream) != hipSuccess)
-    return SSD_ERR_LAUNCH;
-  // 4-wave workgroups (two per CU) for chunks of 64 and 128 tokens; 8 waves
-  // for 256-token chunks, whose row tiles would not fit 4 waves' registers
-  constexpr int W = main_waves<Q>();
-  if (prm.z)
-    hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, F32, IO, W, true>), dim3((unsigned)g2),
-                       dim3(64 * W), 0, stream, prm);
-  else
-    hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, F32, IO, W, false>), dim3((unsigned)g2),
-                       dim3(64 * W), 0, stream, prm);
-  if (hipGetLastError() != hipSuccess) return SSD_ERR_LAUNCH;
-  if (d->ev_main_end && hipEventRecord(static_cast<hipEvent_t>(d->ev_main_end), stream) != hipSuccess)
-    return SSD_ERR_LAUNCH;
-  return SSD_OK;
-}
-
-template <int Q, int N, bool F32>
-ssd_status dispatch_io(const Params &prm, const Plan &pl, hipStream_t s, const ssd_desc *d) {
-  if (d->x_dtype == SSD_BF16) return launch_all<Q, N, F32, IoBF16>(prm, pl, s, d);
-  return launch_all<Q, N, F32, IoF32>(prm, pl, s, d);
-}
-
-template <int Q, int N>
-ssd_status dispatch_mma(const Params &prm, const Plan &pl, hipStream_t s, const ssd_desc *d) {
-  if (d->mma == SSD_MMA_F32) return dispatch_io<Q, N, true>(prm, pl, s, d);
-  return dispatch_io<Q, N, false>(prm, pl, s, d);
-}
-
-template <int Q>
-ssd_status dispatch_n(const Params &prm, const Plan &pl, hipStream_t s, const ssd_desc *d) {
-  if (d->dstate == 64) return dispatch_mma<Q, 64>(prm, pl, s, d);
-  return dispatch_mma<Q, 128>(prm, pl, s, d);
-}
-
 // The forward with its workspace given explicitly (the caller's buffer, or
 // the static scratch of ssd_fwd_noalloc); `d->workspace` is not read here.
 ssd_status fwd_impl(const void *x, const float *dt, const float *A, const void *B, const void *C,
@@ -1365,9 +146,9 @@ ssd_status fwd_impl(const void *x, const float *dt, const float *A, const void *
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (chunk) {
-    case 64: return dispatch_n<64>(prm, pl, s, d);
-    case 128: return dispatch_n<128>(prm, pl, s, d);
-    default: return dispatch_n<256>(prm, pl, s, d);
+    case 64: return launch_q64(prm, pl, s, d);
+    case 128: return launch_q128(prm, pl, s, d);
+    default: return launch_q256(prm, pl, s, d);
   }
 }
 
@@ -1398,7 +179,9 @@ void *scratch_ptr(int dev) {
   return s.ptr;
 }
 
-}  // namespace
+}  // namespace ssd_fwd_impl
+
+using namespace ssd_fwd_impl;
 
 extern "C" {
 
@@ -1413,6 +196,7 @@ void ssd_desc_init(ssd_desc *d, int64_t batch, int64_t seqlen, int64_t nheads, i
   d->dstate = dstate;
   d->ngroups = ngroups;
   d->x_dtype = SSD_F32;
+  d->bc_dtype = SSD_F32;
   d->z_dtype = SSD_F32;
   d->out_dtype = SSD_F32;
   d->mma = SSD_MMA_F16;

@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(bnd.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), f"{name} not exported"
-    assert lib.ssd_abi_version() == 3
+    assert lib.ssd_abi_version() == 4
 
 
 def test_desc_layout_matches_c(lib):
@@ -57,7 +57,7 @@ def test_desc_layout_matches_c(lib):
                                                           bnd.SSD_MMA_F16)
     assert d.dt_min == 0.0 and math.isinf(d.dt_max)
     assert d.z is None and d.dt_bias is None and d.initial_state is None and d.workspace is None
-    assert d.workspace_bytes == 0 and d.chunks_per_wg == 0 and d.reserved == 0
+    assert d.workspace_bytes == 0 and d.chunks_per_wg == 0 and d.bc_dtype == bnd.SSD_F32
     assert d.ev_main_begin is None and d.ev_main_end is None and d.cu_seqlens is None
     assert d.packed_tokens == 0 and d.error_flag is None
 
@@ -89,8 +89,8 @@ def _desc(**kw):
 @pytest.mark.parametrize("field,value", [("batch", 0), ("seqlen", 0), ("nheads", 0),
                                          ("headdim", 0), ("dstate", -1), ("ngroups", 0),
                                          ("ngroups", 3), ("x_dtype", 9), ("z_dtype", -1),
-                                         ("out_dtype", 7), ("mma", 1), ("chunks_per_wg", -2),
-                                         ("reserved", 1)])
+                                         ("out_dtype", 7), ("mma", 3), ("mma", -1),
+                                         ("chunks_per_wg", -2), ("bc_dtype", 5)])
 def test_invalid_descriptor_fields(lib, field, value):
     d = _desc()
     setattr(d, field, value)
@@ -126,6 +126,7 @@ def test_misaligned_pointer(lib, arg):
 @pytest.mark.parametrize("kw,chunk", [({"P": 32}, 64), ({"P": 128}, 64), ({"N": 32}, 64),
                                       ({"N": 256}, 64), ({}, 32), ({}, 512), ({}, 100),
                                       ({"x_dtype": bnd.SSD_F16}, 64),
+                                      ({"bc_dtype": bnd.SSD_F16}, 64),
                                       ({"out_dtype": bnd.SSD_F16}, 64)])
 def test_unsupported(lib, kw, chunk):
     assert _call(lib, _desc(**kw), chunk=chunk) == bnd.SSD_ERR_UNSUPPORTED

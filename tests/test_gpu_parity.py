@@ -3,6 +3,9 @@
 Bar (per output tensor): max|gpu - oracle| <= tol * max|oracle|, with
 tol = 2e-3 on the fp16-operand MFMA path and 1e-4 on the all-fp32 check
 path; the same bound applies to final_state against max|final_state|.
+The bf16-operand path gets 8 x the fp16 bound, 1.6e-2: the same multiple
+of its unit roundoff (2^-8 for bf16's 8 significant bits against 2^-11 for
+fp16's 11), since every operand rounding scales with it.
 NRMSE and cosine similarity are printed alongside.
 """
 import math
@@ -17,7 +20,7 @@ from workloads import WORKLOADS, make_inputs, random_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f16": 2e-3, "f32": 1e-4}
+TOL = {"f16": 2e-3, "bf16": 8 * 2e-3, "f32": 1e-4}
 
 
 def _say(msg):
@@ -84,7 +87,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("mma", ["f16", "f32"])
+@pytest.mark.parametrize("mma", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_shapes(gpu_lib, case, mma):
     name, Bsz, L, H, N, G, Q, hD, hz, hh, hb, io, limit = case
@@ -99,7 +102,7 @@ def test_small_shapes(gpu_lib, case, mma):
         assert_close(fin, ref_fin, TOL[mma], f"final_state (chunks_per_wg={cpw})")
 
 
-@pytest.mark.parametrize("mma", ["f16", "f32"])
+@pytest.mark.parametrize("mma", ["f16", "bf16", "f32"])
 def test_tiny_workload(gpu_lib, mma):
     w = WORKLOADS["tiny"]
     _say(f"[case] tiny workload {w.shape_str()} mma={mma}")
@@ -301,5 +304,64 @@ def test_full_workload_sampled_pairs(gpu_lib, name):
         ref_out, ref_fin = oracle_run(s)
         assert_close(out[b:b + 1, :, h:h + 1], ref_out, TOL["f16"], f"out (b={b}, h={h})")
         assert_close(fin[b:b + 1, h:h + 1], ref_fin, TOL["f16"], f"final (b={b}, h={h})")
+    del d, out, fin
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ bf16 operands and storage
+
+@pytest.mark.parametrize("mma", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("x_io,bc_io", [("f32", "bf16"), ("bf16", "f32")])
+def test_mixed_storage_dtypes(gpu_lib, mma, x_io, bc_io):
+    """x in one storage dtype, B and C in another (the descriptor's x_dtype
+    and bc_dtype): the oracle reads the same stored values."""
+    _say(f"[case] mixed storage x={x_io} B/C={bc_io} mma={mma}")
+    d = random_inputs(2, 333, 4, 64, 128, 2, seed=1300, has_D=True, has_z=True, has_h0=True,
+                      dt_bias=True)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    d["x"] = d["x"].to(dt[x_io])
+    d["B"], d["C"] = d["B"].to(dt[bc_io]), d["C"].to(dt[bc_io])
+    ref_out, ref_fin = oracle_run(d)
+    for Q, cpw in ((64, 1), (128, 0), (256, 0)):
+        out, fin = gpu_run(gpu_lib, d, Q, mma=mma, chunks_per_wg=cpw)
+        assert_close(out, ref_out, TOL[mma], f"out Q={Q}")
+        assert_close(fin, ref_fin, TOL[mma], f"final_state Q={Q}")
+
+
+@pytest.mark.parametrize("scale", [1e5, 1e-5])
+def test_bf16_operands_cover_magnitudes_outside_fp16(gpu_lib, scale):
+    """bf16 inputs scaled by 1e5 (values and products far above fp16's 65504)
+    or 1e-5 (products below fp16's smallest subnormal, 6e-8): the bf16-operand
+    path keeps its bound; the fp16-operand path, whose operands must lie in
+    fp16's range, overflows (1e5) or loses the products (1e-5)."""
+    _say(f"[case] bf16 storage scaled by {scale:g}")
+    d = random_inputs(1, 300, 4, 64, 128, 2, seed=1310, has_D=False, has_h0=False,
+                      io_dtype="bf16", scale=scale)
+    ref_out, ref_fin = oracle_run(d)
+    for Q in (64, 128, 256):
+        out, fin = gpu_run(gpu_lib, d, Q, mma="bf16")
+        assert_close(out, ref_out, TOL["bf16"], f"out Q={Q} (bf16 operands)")
+        assert_close(fin, ref_fin, TOL["bf16"], f"final_state Q={Q} (bf16 operands)")
+    out, _ = gpu_run(gpu_lib, d, 128, mma="f16")
+    if scale > 1:
+        assert not np.isfinite(out).all(), "fp16 operands were expected to overflow"
+    else:
+        rel = float(np.abs(out - ref_out).max() / np.abs(ref_out).max())
+        _say(f"    fp16 operands: max_err/max_ref={rel:.3e}")
+        assert rel > 10 * TOL["f16"], "fp16 operands were expected to lose these products"
+
+
+def test_gated_workload_on_bf16_operands(gpu_lib):
+    """The gated bf16 workload [2,8192,128,64,128,256,8] on bf16 MFMA operands,
+    in the plan the benchmark uses, with sampled (b, h) sequences."""
+    w = WORKLOADS["gated"]
+    _say(f"[case] gated workload {w.shape_str()} mma=bf16")
+    d = make_inputs(w)
+    out, fin = gpu_run(gpu_lib, d, w.chunk, mma="bf16")
+    for b, h in sorted({(0, 0), (1, 127), (1, 64), (0, 17)}):
+        s = _pair_slice(d, b, h, w.nheads, w.ngroups)
+        ref_out, ref_fin = oracle_run(s)
+        assert_close(out[b:b + 1, :, h:h + 1], ref_out, TOL["bf16"], f"out (b={b}, h={h})")
+        assert_close(fin[b:b + 1, h:h + 1], ref_fin, TOL["bf16"], f"final (b={b}, h={h})")
     del d, out, fin
     torch.cuda.empty_cache()
