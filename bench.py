@@ -256,6 +256,51 @@ def cpu_baseline(w: Workload, budget_s: float):
             "one_thread_fp32": one, "host": host_cpu()}
 
 
+def calibrate(dev: str) -> dict:
+    """What this GPU delivers, next to the published peaks: a 1 GiB device
+    copy (torch), a 1 GiB streaming read and back-to-back fp16 MFMAs (the
+    calibration kernels of libssd_calib.so), each timed with events on the
+    current stream after a warm-up."""
+    from mamba_ssd_chunked_04_amd.build import CALIB_LIB
+    lib = ctypes.CDLL(CALIB_LIB)
+    lib.ssd_calib_mfma_f16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.ssd_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, device=dev)
+    dst = torch.empty_like(src)
+    blocks_read, blocks_mfma, iters = 2048, 1024, 2000
+    out = torch.empty(max(blocks_read, blocks_mfma) * 256, device=dev)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"calibration kernel failed: HIP error {rc}")
+
+    t_copy = timed(lambda: dst.copy_(src), 5)
+    t_read = timed(lambda: check(lib.ssd_calib_read(src.data_ptr(), nbytes, out.data_ptr(),
+                                                    blocks_read, ctypes.c_void_p(stream))), 5)
+    t_mfma = timed(lambda: check(lib.ssd_calib_mfma_f16(out.data_ptr(), blocks_mfma, iters,
+                                                        ctypes.c_void_p(stream))), 3)
+    del src, dst, out
+    flops = blocks_mfma * 4 * iters * 8 * 2 * 16 * 16 * 32
+    return {"hbm_copy_gbs": 2 * nbytes / t_copy / 1e9, "hbm_read_gbs": nbytes / t_read / 1e9,
+            "mfma_f16_tflops": flops / t_mfma / 1e12,
+            "how": "1 GiB device copy (read + write bytes), 1 GiB streaming read, "
+                   f"{blocks_mfma} x 256-thread blocks of back-to-back 16x16x32 fp16 MFMAs"}
+
+
 def copy_calibration(mb: int, dev: str) -> None:
     """A plain device copy of known size, run three times: the reference
     kernel that scales the HBM byte counters."""
@@ -594,7 +639,8 @@ def main(argv=None):
                     help="workload; 'page' is the conv1d test shape of --op causal_conv1d")
     ap.add_argument("--op", default="ssd_fwd", choices=["ssd_fwd", "ssd_bwd", "rmsnorm_gated",
                                                         "causal_conv1d"])
-    ap.add_argument("--mma", default="f16", choices=["f16", "f32"])
+    ap.add_argument("--mma", default="auto", choices=["auto", "f16", "bf16", "f32"],
+                    help="MFMA operand precision; auto = bf16 for bf16 storage, else f16")
     ap.add_argument("--chunks-per-wg", type=int, default=0)
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = auto)")
     ap.add_argument("--split-samples", type=int, default=20,
@@ -602,6 +648,8 @@ def main(argv=None):
                          "whole call and its main-pass kernel (the per-kernel split)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip measuring the GPU's own copy, read and MFMA peaks")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before warmup, run a plain device copy of this many MB three times "
                          "(a known-size reference kernel for HBM byte counters)")
@@ -630,6 +678,8 @@ def main(argv=None):
     dev = "cuda:0"
     if args.op == "rmsnorm_gated":
         return norm_main(args, w)
+    if args.mma == "auto":
+        args.mma = "bf16" if w.io_dtype == "bf16" else "f16"
     print(f"[bench] workload {w.name} {w.shape_str()} mma={args.mma}", file=sys.stderr, flush=True)
 
     # rotating input/output sets: total footprint > 2 x 256 MB Infinity Cache
@@ -712,7 +762,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (tok_s / PAGE_TOKENS_PER_S[w.name]) if w.name in PAGE_TOKENS_PER_S else None,
-        "dtype": "f16" if args.mma == "f16" else "f32",
+        "dtype": args.mma,
         "data": "synthetic",
         "config": {"workload": f"{w.name} {w.shape_str()}", "B": w.batch, "L": w.seqlen,
                    "H": w.nheads, "P": w.headdim, "N": w.dstate, "chunk": w.chunk,
@@ -735,6 +785,17 @@ def main(argv=None):
                  "hbm_frac": abytes / (wall / K) / 1e9 / HBM_PEAK_GBS,
                  "tflops": flops / (wall / K) / 1e12},
     }
+    if not args.no_calibration:
+        print("[bench] calibrating the GPU's delivered peaks", file=sys.stderr, flush=True)
+        try:
+            cal = calibrate(dev)
+        except (OSError, RuntimeError) as e:          # library missing or a kernel refused
+            cal = {"error": str(e)}
+        if "hbm_read_gbs" in cal:
+            rec["roofline"]["calibrated"] = {
+                "peak": cal["hbm_read_gbs"], "unit": "GB/s", "frac": achieved / cal["hbm_read_gbs"],
+                "of": "this GPU's measured streaming-read rate"}
+        rec["calibration"] = cal
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_baseline_seconds)
