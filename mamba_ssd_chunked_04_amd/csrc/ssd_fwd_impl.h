@@ -143,6 +143,11 @@ struct IoF32 {
   static __device__ __forceinline__ float load1(rsrc_t r, uint32_t off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off * 4, 0, 0));
   }
+  typedef float raw2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ raw2 load2(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(raw2, __builtin_amdgcn_raw_buffer_load_b64(r, off * 4, 0, 0));
+  }
+  static __device__ __forceinline__ float cvt2(const raw2 &v, int e) { return v[e]; }
 };
 
 struct IoBF16 {
@@ -169,6 +174,13 @@ struct IoBF16 {
   }
   static __device__ __forceinline__ float load1(rsrc_t r, uint32_t off) {
     return bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off * 2, 0, 0));
+  }
+  typedef uint32_t raw2;
+  static __device__ __forceinline__ raw2 load2(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off * 2, 0, 0);
+  }
+  static __device__ __forceinline__ float cvt2(const raw2 &v, int e) {
+    return bf16_bits_to_f32(e ? (v >> 16) : (v & 0xffffu));
   }
 };
 
@@ -437,11 +449,16 @@ template <int N, class IO, int T>
 struct BlockRaw {
   static constexpr int NG = N / 4;                  // column groups of B
   static constexpr int UB = 16 * NG;                // B units
-  static constexpr int UX = 16 * (kP / 4);          // x units
+  // x units: 4 tokens x 4 columns, or 4 tokens x 2 columns when the
+  // workgroup has at least twice as many threads as 4-column units (every
+  // thread then holds one unit, in half the registers)
+  static constexpr bool XPAIR = T >= 2 * 16 * (kP / 4);
+  static constexpr int UX = XPAIR ? 16 * (kP / 2) : 16 * (kP / 4);
   static constexpr int KB_ = (UB + T - 1) / T;      // B units per thread
   static constexpr int KX = (UX + T - 1) / T;       // x units per thread
   typename IO::BC::raw4 b[KB_][4];
-  typename IO::X::raw4 x[KX][4];
+  typename IO::X::raw4 x[XPAIR ? 1 : KX][XPAIR ? 1 : 4];
+  typename IO::X::raw2 x2[XPAIR ? KX : 1][XPAIR ? 4 : 1];
 };
 
 // Staging unit u -> (token quad rg in 0..15, column quad cg).  Every 64
@@ -486,8 +503,12 @@ __device__ __forceinline__ void load_block(const SeqView<N, IO> &sv, uint32_t tb
     int rg, pg;
     unit_of(u, rg, pg);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      r.x[k][e] = IO::X::load4(sv.x, ok ? sv.xoff(tb + 4 * rg + e, 4 * pg) : kNoElem);
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (BR::XPAIR)
+        r.x2[k][e] = IO::X::load2(sv.x, ok ? sv.xoff(tb + 4 * rg + e, 2 * pg) : kNoElem);
+      else
+        r.x[k][e] = IO::X::load4(sv.x, ok ? sv.xoff(tb + 4 * rg + e, 4 * pg) : kNoElem);
+    }
   }
 }
 
@@ -539,15 +560,25 @@ __device__ __forceinline__ void store_block(const BlockRaw<N, IO, T> &r, int jb,
       int rg, pg;
       unit_of(u, rg, pg);
       const int r0 = 4 * rg;
-      f32x4 v[4];
+      if constexpr (BR::XPAIR) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = IO::X::cvt4(r.x[k][e]);
+        for (int c = 0; c < 2; ++c) {
+          quad q;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        quad q;
+          for (int e = 0; e < 4; ++e) q[e] = (E)IO::X::cvt2(r.x2[k][e], c);
+          *reinterpret_cast<quad *>(&sXT[(2 * pg + c) * LDJ + r0]) = q;
+        }
+      } else {
+        f32x4 v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] = (E)v[e][c];
-        *reinterpret_cast<quad *>(&sXT[(4 * pg + c) * LDJ + r0]) = q;
+        for (int e = 0; e < 4; ++e) v[e] = IO::X::cvt4(r.x[k][e]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          quad q;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[e] = (E)v[e][c];
+          *reinterpret_cast<quad *>(&sXT[(4 * pg + c) * LDJ + r0]) = q;
+        }
       }
     }
   }
@@ -883,18 +914,12 @@ __global__ __launch_bounds__(256 * HW) void ssd_group_state_kernel(Params p) {
   // the aggregate, in the main pass's register order
   const int64_t slot = bh * (p.ngroups - 1) + j;
   float *dst = p.grp_state + slot * (int64_t)(kP * N);
+  // (the four rows of a fragment are consecutive in the record, and
+  // consecutive lanes' fragments adjacent: one coalesced 16-byte store each)
   constexpr int WM = main_waves<Q>();
-  if (WM == 4) {
 #pragma unroll
-    for (int t = 0; t < NN; ++t)
-      *reinterpret_cast<f32x4 *>(dst + (t * 256 + tid) * 4) = sacc[t];
-  } else {
-#pragma unroll
-    for (int t = 0; t < NN; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dst[rec_index<N, WM>(16 * wl + 4 * lq + r, 16 * t + lr)] = sacc[t][r];
-  }
+  for (int t = 0; t < NN; ++t)
+    *reinterpret_cast<f32x4 *>(dst + rec_index<N, WM>(16 * wl + 4 * lq, 16 * t + lr)) = sacc[t];
   if (tid == 0) p.grp_lam[slot] = lgrp;
 }
 
