@@ -40,9 +40,11 @@ extern "C" {
 typedef enum {
   SSD_OK = 0,
   SSD_ERR_INVALID_ARG = 1,  /* NULL required pointer, dim < 1, H % G != 0,
-                               misaligned pointer (cu_seqlens: 4 bytes),
+                               misaligned pointer (cu_seqlens, and dt of
+                               ssd_fwd: 4 bytes),
                                bad dtype/mma code, final_state NULL
-                               while requested                        */
+                               while requested, a token stride below its
+                               dense value or not a multiple of 16 bytes */
   SSD_ERR_UNSUPPORTED = 2,  /* valid but not compiled: headdim != 64,
                                dstate not in {64,128}, chunk not in
                                {64,128,256}, fp16 storage, or one batch
@@ -137,6 +139,21 @@ typedef struct ssd_desc {
                                 never clears it: the caller zeroes it and
                                 reads it after synchronising.  Ignored for
                                 dense calls                               */
+  /* Token strides, in elements: the distance between consecutive tokens of
+     x, of B (and C, the same), of z and of dt.  0 means the dense layout
+     (H*P, G*N, H*P and H).  A larger stride reads these tensors as views of
+     wider token-major rows in place -- for example x, B and C as column
+     ranges of one conv output [B, L, H*P + 2*G*N], or z and dt inside a
+     projection's output -- while out stays dense [B, L, H, P].  Batch row b
+     starts b*L tokens after row 0 (for packed calls, the offsets count
+     tokens).  Strides of x, B/C and z must be multiples of 16 bytes; each
+     batch row's span (seqlen * stride * element size) must stay below 2 GiB.
+     dt is read one element at a time: its pointer needs 4-byte alignment
+     only, so it may start at any column of a wider fp32 row. */
+  int64_t x_stride;
+  int64_t bc_stride;
+  int64_t z_stride;
+  int64_t dt_stride;
 } ssd_desc;
 
 /* Fills `d` with defaults for the given shape: fp32 storage (x, B, C, z,
@@ -205,6 +222,7 @@ ssd_status ssd_fwd_noalloc(const void *x, const float *dt, const float *A,
 ssd_status ssd_bwd_workspace_size(const ssd_desc *d, int64_t chunk, size_t *bytes);
 
 /* SSD backward: gradients of L = <dout, out> + <dfinal_state, final_state>
+ * (dense tensors only: the descriptor's token strides must be 0)
  * for the forward ssd_fwd computes, in fp32.  The scope is the
  * one the page "Mamba-2 SSD for Ascend NPU" gives its first backward
  * ("AscendC training", "Limitations and roadmap"): contiguous
@@ -277,13 +295,38 @@ ssd_status ssd_causal_conv1d(const float *x, const float *w, const float *bias,
                              int64_t seqlen, int64_t width, int activation,
                              float *out, float *final_state, void *stream);
 
+/* The same convolution over token-major tensors, the layout the input
+ * projection writes (page "ops-transformer MambaV2 算子套件", §1.4: x, B and
+ * C leave the projection as [B, S, channels] before the conv):
+ *
+ *   out[b,t,d] = act(bias[d] + sum_{k<W} w[d,k] * xx[b,t-(W-1)+k,d])
+ *
+ *   x           [B, S, *] fp32: token (b, t) holds channels 0..D-1 at
+ *               x + (b*S + t)*x_stride (x_stride >= D), so x may be a column
+ *               range of a wider token-major row; 16-byte aligned
+ *   out         [B, S, D] fp32 dense, 16-byte aligned
+ *   w [D, W], bias [D] or NULL, x_prev / final_state [B, D, W-1] or NULL as
+ *   for ssd_causal_conv1d; final_state may be x_prev itself when S <= 32.
+ * Errors: SSD_ERR_INVALID_ARG for a NULL x/w/out, a size < 1, x_stride < D,
+ * activation not 0/1, x or out not 16-byte aligned, another pointer not
+ * 4-byte aligned or a forbidden overlap (out with x or final_state,
+ * final_state with x, or with x_prev beyond the in-place case);
+ * SSD_ERR_UNSUPPORTED for W outside 2..4, D or x_stride not a multiple of
+ * 4, one batch's x or out reaching 2^31 bytes or 2^31 workgroups
+ * (B * ceil(D/256) * ceil(S/128)). */
+ssd_status ssd_causal_conv1d_tokmajor(const float *x, int64_t x_stride, const float *w,
+                                      const float *bias, const float *x_prev, int64_t batch,
+                                      int64_t dim, int64_t seqlen, int64_t width,
+                                      int activation, float *out, float *final_state,
+                                      void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *ssd_status_str(int status);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int ssd_abi_version(void);
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,8 @@ SSD_MMA_F16, SSD_MMA_BF16, SSD_MMA_F32 = 0, 1, 2
 # Every symbol include/ssd_mi355x.h declares.
 EXPORTED_SYMBOLS = ("ssd_desc_init", "ssd_fwd_workspace_size", "ssd_fwd_plan", "ssd_fwd",
                     "ssd_fwd_noalloc", "ssd_bwd_workspace_size", "ssd_bwd", "ssd_rmsnorm_gated",
-                    "ssd_causal_conv1d", "ssd_status_str", "ssd_abi_version")
+                    "ssd_causal_conv1d", "ssd_causal_conv1d_tokmajor", "ssd_status_str",
+                    "ssd_abi_version")
 # include/ssd_mi355x.h: SSD_FWD_NOALLOC_MAX_SCRATCH
 NOALLOC_MAX_SCRATCH = 64 << 20
 
@@ -39,6 +40,8 @@ class SsdDesc(ctypes.Structure):
         ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p),
         ("cu_seqlens", ctypes.c_void_p), ("packed_tokens", ctypes.c_int64),
         ("error_flag", ctypes.c_void_p),
+        ("x_stride", ctypes.c_int64), ("bc_stride", ctypes.c_int64),
+        ("z_stride", ctypes.c_int64), ("dt_stride", ctypes.c_int64),
     ]
 
 
@@ -81,6 +84,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ssd_bwd.restype = c_int
     lib.ssd_causal_conv1d.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, c_int, vp, vp, vp]
     lib.ssd_causal_conv1d.restype = c_int
+    lib.ssd_causal_conv1d_tokmajor.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, i64, c_int, vp,
+                                               vp, vp]
+    lib.ssd_causal_conv1d_tokmajor.restype = c_int
     lib.ssd_status_str.argtypes = [c_int]
     lib.ssd_status_str.restype = ctypes.c_char_p
     lib.ssd_abi_version.argtypes = []
@@ -133,6 +139,28 @@ def _dtype_code(t) -> int:
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _token_stride(t, name: str) -> int:
+    """Elements between consecutive tokens of a [B, L, ...] tensor whose
+    per-token dims are dense and whose batch rows lie L tokens apart (a
+    column range of wider token-major rows, such as x, B or C inside a conv
+    output); 0 when the tensor is contiguous."""
+    if t.is_contiguous():
+        return 0
+    shp, st = t.shape, t.stride()
+    expect = 1
+    for dim in range(t.dim() - 1, 1, -1):
+        if shp[dim] != 1 and st[dim] != expect:
+            raise ValueError(f"{name}: the dims after the token dim must be dense")
+        expect *= shp[dim]
+    # a size-1 axis carries no stride of its own: with one token per row the
+    # batch stride is the token stride
+    ts = st[1] if shp[1] > 1 else (st[0] if shp[0] > 1 else expect)
+    if ts < expect or (shp[0] > 1 and st[0] != shp[1] * ts):
+        raise ValueError(f"{name}: tokens must be at least one row apart and batch rows "
+                         f"L tokens apart")
+    return int(ts)
 
 
 class SsdCall:
@@ -195,6 +223,11 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     ``out`` is float32 unless ``out_dtype`` (float32 or bfloat16) says
     otherwise, whatever the dtype of x, B and C.
 
+    x, B, C, z and dt may be token-strided views (dense per-token dims,
+    batch rows L tokens apart), read in place -- e.g. x, B and C as column
+    ranges of one token-major conv output [B, L, H*P + 2*G*N]; the other
+    tensors must be contiguous.
+
     Packed variable-length sequences: x [1, T, H, P] (dt [1, T, H], B/C
     [1, T, G, N], z like x) with ``cu_seqlens`` an int32 GPU tensor of
     nseq+1 token offsets; initial and final states are then [nseq, H, P, N].
@@ -248,8 +281,17 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
             raise ValueError(f"{name} must have shape {shp}")
     tensors = [x, dt, A, B, C, D, z, dt_bias, initial_states]
     for t in tensors:
-        if t is not None and (t.device != dev or not t.is_contiguous()):
-            raise ValueError("all tensors must be contiguous and on the same GPU")
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+    # x, B, C, z and dt may be token-strided views; the rest dense
+    strides = {"x": _token_stride(x, "x"), "B": _token_stride(B, "B"), "C": _token_stride(C, "C"),
+               "z": _token_stride(z, "z") if z is not None else 0, "dt": _token_stride(dt, "dt")}
+    bc_dense = G * N
+    if (strides["B"] or bc_dense) != (strides["C"] or bc_dense):
+        raise ValueError("B and C must have the same token stride")
+    for t in (A, D, dt_bias, initial_states):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("A, D, dt_bias and initial_states must be contiguous")
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty(Bsz, L, H, P, device=dev, dtype=out_dtype)
@@ -272,6 +314,8 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     desc.dt_min, desc.dt_max = float(dt_limit[0]), float(dt_limit[1])
     desc.z, desc.dt_bias, desc.initial_state = _ptr(z), _ptr(dt_bias), _ptr(initial_states)
     desc.chunks_per_wg = int(chunks_per_wg)
+    desc.x_stride, desc.z_stride, desc.dt_stride = strides["x"], strides["z"], strides["dt"]
+    desc.bc_stride = strides["B"] or strides["C"]
     nbytes = workspace_size(desc, chunk_size)
     if nbytes > 0 and workspace is None and not noalloc:
         workspace = torch.empty(nbytes, device=dev, dtype=torch.uint8)
@@ -388,6 +432,54 @@ def causal_conv1d(x, weight, bias=None, conv_state=None, activation: str = "silu
             _ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state), Bsz, D, S, W, act, _ptr(out),
             _ptr(final_state) if return_final_state else None, ctypes.c_void_p(st)),
             "ssd_causal_conv1d")
+    return (out, final_state) if return_final_state else out
+
+
+def causal_conv1d_tokmajor(x, weight, bias=None, conv_state=None, activation: str = "silu",
+                           out=None, return_final_state: bool = False, final_state=None):
+    """The same conv over token-major x: [B, S, D] float32 GPU tensor whose
+    channels are contiguous and whose batches are S token rows apart (a
+    column range x = proj[..., a:a + D] of a wider [B, S, *] tensor is
+    taken as it is, without a copy).  out: [B, S, D] dense; weight, bias and
+    conv_state as for causal_conv1d (``final_state`` may be ``conv_state``
+    itself when S <= 32).
+    """
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dim() != 3:
+        raise ValueError("x must be a [B, S, D] GPU tensor")
+    Bsz, S, D = x.shape
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32")
+    # token row stride (a size-1 axis carries no stride of its own)
+    xs = x.stride(1) if S > 1 else (x.stride(0) if Bsz > 1 else D)
+    if (D > 1 and x.stride(2) != 1) or (Bsz > 1 and x.stride(0) != S * xs):
+        raise ValueError("x must have contiguous channels and batches S token rows apart")
+    if weight.dim() != 2 or weight.shape[0] != D:
+        raise ValueError("weight must be [D, W]")
+    W = weight.shape[1]
+    if activation not in ("silu", "none", None):
+        raise ValueError(f"activation must be 'silu' or None, got {activation!r}")
+    act = 1 if activation == "silu" else 0
+    if out is None:
+        out = torch.empty(Bsz, S, D, device=x.device, dtype=torch.float32)
+    if return_final_state and final_state is None:
+        final_state = torch.empty(Bsz, D, W - 1, device=x.device, dtype=torch.float32)
+    shapes = ((bias, (D,)), (conv_state, (Bsz, D, W - 1)), (out, (Bsz, S, D)),
+              (final_state if return_final_state else None, (Bsz, D, W - 1)))
+    for t, shp in shapes:
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"expected shape {shp}, got {tuple(t.shape)}")
+    for t in (weight, bias, conv_state, out, final_state):
+        if t is None:
+            continue
+        if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous():
+            raise ValueError("weight, bias, states and out must be contiguous float32 on the GPU of x")
+    with torch.cuda.device(x.device):
+        st = torch.cuda.current_stream(x.device).cuda_stream
+        _raise_for(load_library().ssd_causal_conv1d_tokmajor(
+            _ptr(x), xs, _ptr(weight), _ptr(bias), _ptr(conv_state), Bsz, D, S, W, act,
+            _ptr(out), _ptr(final_state) if return_final_state else None, ctypes.c_void_p(st)),
+            "ssd_causal_conv1d_tokmajor")
     return (out, final_state) if return_final_state else out
 
 

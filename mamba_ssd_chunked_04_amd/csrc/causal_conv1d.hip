@@ -202,6 +202,105 @@ __global__ __launch_bounds__(256) void causal_conv1d_step_kernel(ConvArgs a) {
   if (blk == a.nblk - 1) write_final<W>(a, r, row, lane);
 }
 
+// ------------------------------------------------------------ token-major layout
+// The same convolution on token-major tensors: x [B, S, *] whose token rows
+// are xs elements apart (channels 0..D-1 of each row are read, so x may be a
+// column range of a wider projection output), out [B, S, D] dense, the conv
+// state x_prev / final_state [B, D, W-1] as above.  A wave owns 256 channels
+// (4 consecutive ones per lane) and walks 32 consecutive steps: every load
+// and store of a step is one 1 KB row segment, the W-1 steps before the
+// current one stay in registers, and the W-1 steps before the wave's first
+// step come from x (or x_prev before t = 0).  Eight steps are loaded ahead.
+constexpr int kTokSteps = 32;   // steps per wave
+constexpr int kTokAhead = 8;    // steps loaded ahead
+
+struct TokArgs {
+  const float *x, *w, *bias, *x_prev;
+  float *out, *fin;
+  int64_t batch, dim, S, xs;
+  int act;
+  uint32_t cblk, sblk;  // 256-channel blocks, 128-step blocks (four waves each)
+};
+
+template <int W>
+__global__ __launch_bounds__(256) void causal_conv1d_tok_kernel(TokArgs a) {
+  const uint32_t n = blockIdx.x;
+  const uint32_t sb = n % a.sblk, cb = (n / a.sblk) % a.cblk;
+  const int64_t b = n / (a.sblk * a.cblk);
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int64_t c = 256 * (int64_t)cb + 4 * lane;         // this lane's first channel
+  const bool live = c < a.dim;                             // D % 4 == 0: all four or none
+  const int64_t t0 = (int64_t)sb * 4 * kTokSteps + wave * kTokSteps;
+  if (t0 >= a.S) return;
+  const rsrc_t rx = make_rsrc(a.x + b * a.S * a.xs, (uint32_t)(a.S * a.xs * 4));
+  const rsrc_t ro = make_rsrc(a.out + b * a.S * a.dim, (uint32_t)(a.S * a.dim * 4));
+  auto xoff = [&](int64_t t) -> uint32_t {
+    return (live && t >= 0 && t < a.S) ? (uint32_t)((t * a.xs + c) * 4) : kOOB;
+  };
+  // taps and bias of the four channels
+  f32x4 tap[W], bias = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < W; ++j) tap[j][i] = live ? a.w[(c + i) * W + j] : 0.f;
+    if (a.bias && live) bias[i] = a.bias[c + i];
+  }
+  // the W-1 steps before t0: from x, or from the conv state before t = 0
+  f32x4 win[W];  // win[W-1] is filled with the current step
+#pragma unroll
+  for (int j = 0; j < W - 1; ++j) {
+    const int64_t t = t0 - (W - 1) + j;
+    if (t >= 0) {
+      win[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff(t), 0, 0));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        win[j][i] = (a.x_prev && live) ? a.x_prev[((b * a.dim) + c + i) * (W - 1) + (t + W - 1)] : 0.f;
+    }
+  }
+  f32x4 buf[kTokAhead];
+#pragma unroll
+  for (int k = 0; k < kTokAhead; ++k)
+    buf[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff(t0 + k), 0, kStream));
+#pragma unroll
+  for (int g = 0; g < kTokSteps / kTokAhead; ++g) {
+#pragma unroll
+    for (int k = 0; k < kTokAhead; ++k) {
+      const int64_t t = t0 + g * kTokAhead + k;
+      win[W - 1] = buf[k];
+      if (g + 1 < kTokSteps / kTokAhead)
+        buf[k] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff(t + kTokAhead), 0, kStream));
+      // bias, then the taps oldest first (the channel-major kernels' order)
+      f32x4 acc = bias;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < W; ++j) acc[i] = fmaf(tap[j][i], win[j][i], acc[i]);
+        if (a.act) acc[i] = silu(acc[i]);
+      }
+      const uint32_t oo = (live && t < a.S) ? (uint32_t)((t * a.dim + c) * 4) : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro, oo, 0, kStream);
+      // the final conv state: the last W-1 steps of x (x_prev ++ x)
+      if (t == a.S - 1 && a.fin && live) {
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a.fin[((b * a.dim) + c + i) * (W - 1) + j] = win[j + 1][i];
+      }
+#pragma unroll
+      for (int j = 0; j < W - 1; ++j) win[j] = win[j + 1];
+    }
+  }
+}
+
+template <int W>
+ssd_status launch_tok(const TokArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.batch * a.cblk * a.sblk));
+  hipLaunchKernelGGL((causal_conv1d_tok_kernel<W>), grid, dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_LAUNCH;
+}
+
 template <int W>
 ssd_status launch(const ConvArgs &a, bool vec, hipStream_t s) {
   const dim3 grid((unsigned)((a.rows + 3) / 4 * a.nblk));
@@ -258,4 +357,52 @@ extern "C" ssd_status ssd_causal_conv1d(const float *x, const float *w, const fl
   if (width == 2) return launch<2>(a, vec, s);
   if (width == 3) return launch<3>(a, vec, s);
   return launch<4>(a, vec, s);
+}
+
+extern "C" ssd_status ssd_causal_conv1d_tokmajor(const float *x, int64_t x_stride, const float *w,
+                                                 const float *bias, const float *x_prev,
+                                                 int64_t batch, int64_t dim, int64_t seqlen,
+                                                 int64_t width, int activation, float *out,
+                                                 float *final_state, void *stream) {
+  if (!x || !w || !out) return SSD_ERR_INVALID_ARG;
+  if (batch < 1 || dim < 1 || seqlen < 1 || width < 1 || x_stride < dim) return SSD_ERR_INVALID_ARG;
+  if (activation != 0 && activation != 1) return SSD_ERR_INVALID_ARG;
+  const float *ptrs[] = {w, bias, x_prev, final_state};
+  for (const float *p : ptrs)
+    if (p && !aligned(p, 4)) return SSD_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(out, 16)) return SSD_ERR_INVALID_ARG;
+  if (width < 2 || width > 4 || dim % 4 != 0 || x_stride % 4 != 0) return SSD_ERR_UNSUPPORTED;
+  const int64_t cblk = (dim + 255) / 256, sblk = (seqlen + 4 * kTokSteps - 1) / (4 * kTokSteps);
+  if (seqlen * x_stride * 4 >= ((int64_t)1 << 31) || seqlen * dim * 4 >= ((int64_t)1 << 31) ||
+      batch * cblk * sblk >= ((int64_t)1 << 31))
+    return SSD_ERR_UNSUPPORTED;
+  // out must not overlap x (rows of neighbours would be overwritten); the
+  // state may be updated in place only when one wave covers every step (the
+  // wave that reads x_prev is then the one that writes final_state)
+  if (overlap(out, batch * seqlen * dim, x, (batch * seqlen - 1) * x_stride + dim))
+    return SSD_ERR_INVALID_ARG;
+  const int64_t ns = batch * dim * (width - 1);
+  if (overlap(final_state, ns, x_prev, ns) && !(final_state == x_prev && seqlen <= kTokSteps))
+    return SSD_ERR_INVALID_ARG;
+  if (overlap(final_state, ns, x, (batch * seqlen - 1) * x_stride + dim) ||
+      overlap(out, batch * seqlen * dim, final_state, ns))
+    return SSD_ERR_INVALID_ARG;
+  TokArgs a;
+  a.x = x;
+  a.w = w;
+  a.bias = bias;
+  a.x_prev = x_prev;
+  a.out = out;
+  a.fin = final_state;
+  a.batch = batch;
+  a.dim = dim;
+  a.S = seqlen;
+  a.xs = x_stride;
+  a.act = activation;
+  a.cblk = (uint32_t)cblk;
+  a.sblk = (uint32_t)sblk;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (width == 2) return launch_tok<2>(a, s);
+  if (width == 3) return launch_tok<3>(a, s);
+  return launch_tok<4>(a, s);
 }

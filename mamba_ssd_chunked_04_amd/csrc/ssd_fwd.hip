@@ -36,6 +36,16 @@ ssd_status check_shape(const ssd_desc *d, int64_t chunk) {
   if (d->x_dtype == SSD_F16 || d->bc_dtype == SSD_F16 || d->z_dtype == SSD_F16 ||
       d->out_dtype == SSD_F16)
     return SSD_ERR_UNSUPPORTED;
+  // token strides: 0 (dense) or at least the dense row, 16-byte multiples
+  const int64_t xe = d->x_dtype == SSD_BF16 ? 2 : 4, be = d->bc_dtype == SSD_BF16 ? 2 : 4;
+  const int64_t ze = d->z_dtype == SSD_BF16 ? 2 : 4;
+  if (d->x_stride < 0 || d->bc_stride < 0 || d->z_stride < 0 || d->dt_stride < 0)
+    return SSD_ERR_INVALID_ARG;
+  if ((d->x_stride && (d->x_stride < d->nheads * d->headdim || (d->x_stride * xe) % 16)) ||
+      (d->bc_stride && (d->bc_stride < d->ngroups * d->dstate || (d->bc_stride * be) % 16)) ||
+      (d->z_stride && (d->z_stride < d->nheads * d->headdim || (d->z_stride * ze) % 16)) ||
+      (d->dt_stride && d->dt_stride < d->nheads))
+    return SSD_ERR_INVALID_ARG;
   if (d->headdim != kP) return SSD_ERR_UNSUPPORTED;
   if (d->dstate != 64 && d->dstate != 128) return SSD_ERR_UNSUPPORTED;
   if (!is_supported_chunk(chunk)) return SSD_ERR_UNSUPPORTED;
@@ -44,8 +54,13 @@ ssd_status check_shape(const ssd_desc *d, int64_t chunk) {
   if (d->batch > (1 << 20) || d->nheads > (1 << 20) || d->seqlen > ((int64_t)1 << 31))
     return SSD_ERR_UNSUPPORTED;
   const int64_t row_limit = (int64_t)1 << 31;
-  if (d->seqlen * d->nheads * d->headdim * 4 >= row_limit ||
-      d->seqlen * d->ngroups * d->dstate * 4 >= row_limit)
+  const int64_t xs = d->x_stride ? d->x_stride : d->nheads * d->headdim;
+  const int64_t bs = d->bc_stride ? d->bc_stride : d->ngroups * d->dstate;
+  const int64_t zs = d->z_stride ? d->z_stride : d->nheads * d->headdim;
+  const int64_t dts = d->dt_stride ? d->dt_stride : d->nheads;
+  if (d->seqlen * d->nheads * d->headdim * 4 >= row_limit || d->seqlen * xs * 4 >= row_limit ||
+      d->seqlen * bs * 4 >= row_limit || d->seqlen * zs * 4 >= row_limit ||
+      d->seqlen * dts * 4 >= row_limit)
     return SSD_ERR_UNSUPPORTED;
   return SSD_OK;
 }
@@ -100,7 +115,7 @@ ssd_status fwd_impl(const void *x, const float *dt, const float *A, const void *
   if (!x || !dt || !A || !B || !C || !out) return SSD_ERR_INVALID_ARG;
   if (return_final_state && !final_state) return SSD_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(out) ||
-      (d->z && !aligned16(d->z)) || !aligned16(dt) ||
+      (d->z && !aligned16(d->z)) || ((uintptr_t)dt & 3u) != 0 ||
       (d->initial_state && !aligned16(d->initial_state)) ||
       (return_final_state && !aligned16(final_state)) ||
       ((uintptr_t)d->cu_seqlens & 3u) != 0 || ((uintptr_t)d->error_flag & 3u) != 0)
@@ -128,6 +143,10 @@ ssd_status fwd_impl(const void *x, const float *dt, const float *A, const void *
   prm.cu_seqlens = d->cu_seqlens;
   prm.error_flag = d->cu_seqlens ? d->error_flag : nullptr;
   prm.packed_tokens = d->cu_seqlens ? d->packed_tokens : 0;
+  prm.xs = d->x_stride ? d->x_stride : d->nheads * d->headdim;
+  prm.bs = d->bc_stride ? d->bc_stride : d->ngroups * d->dstate;
+  prm.zs = d->z_stride ? d->z_stride : d->nheads * d->headdim;
+  prm.dts = d->dt_stride ? d->dt_stride : d->nheads;
   prm.batch = d->batch;
   prm.L = d->seqlen;
   prm.Q = (int)chunk;

@@ -209,6 +209,7 @@ struct Params {
   const int32_t *cu_seqlens;  // packed calls: [batch+1] token offsets, else NULL
   int32_t *error_flag;        // packed calls: set to 1 on offsets that break the contract
   int64_t packed_tokens;      // packed calls: T when known (offsets are clamped to it), else 0
+  int64_t xs, bs, zs, dts;    // elements between consecutive tokens of x, B/C, z, dt
   int64_t batch, L, H, G, nc, ngroups, cpg;
   int Q;
   float dt_min, dt_max;
@@ -290,26 +291,32 @@ __device__ __forceinline__ int64_t row_groups(const Params &p, int64_t len) {
   return ng < 1 ? 1 : ng;
 }
 
-// Buffer resources and element offsets of one (b, h) sequence.
+// Buffer resources and element offsets of one (b, h) sequence.  Tokens of
+// x, B/C (and z, dt) are xs, bs (zs, dts) elements apart: the dense layouts
+// [.., H, P] and [.., G, N] or strided views of wider token-major rows (such
+// as a conv output holding x, B and C side by side).  out is always dense.
 template <int N, class IO>
 struct SeqView {
   rsrc_t x, B, C;
-  uint32_t H, G, h, g;
+  uint32_t H, G, h, g, xs, bs, dts;
   __device__ __forceinline__ SeqView(const Params &p, const RowSpan &rs, int64_t h_, int64_t g_) {
     const uint64_t L = (uint64_t)rs.len, t0 = (uint64_t)rs.start;
     H = (uint32_t)p.H;
     G = (uint32_t)p.G;
     h = (uint32_t)h_;
     g = (uint32_t)g_;
-    const uint64_t lhp = L * p.H * kP, lgn = L * p.G * N;
-    const uint64_t ohp = t0 * p.H * kP, ogn = t0 * p.G * N;
-    constexpr int xs = IO::X::esz, bs = IO::BC::esz;
-    x = make_rsrc(static_cast<const char *>(p.x) + ohp * xs, (uint32_t)(lhp * xs));
-    B = make_rsrc(static_cast<const char *>(p.B) + ogn * bs, (uint32_t)(lgn * bs));
-    C = make_rsrc(static_cast<const char *>(p.C) + ogn * bs, (uint32_t)(lgn * bs));
+    xs = (uint32_t)p.xs;
+    bs = (uint32_t)p.bs;
+    dts = (uint32_t)p.dts;
+    constexpr int xe = IO::X::esz, be = IO::BC::esz;
+    x = make_rsrc(static_cast<const char *>(p.x) + t0 * p.xs * xe, (uint32_t)(L * p.xs * xe));
+    B = make_rsrc(static_cast<const char *>(p.B) + t0 * p.bs * be, (uint32_t)(L * p.bs * be));
+    C = make_rsrc(static_cast<const char *>(p.C) + t0 * p.bs * be, (uint32_t)(L * p.bs * be));
   }
-  __device__ __forceinline__ uint32_t xoff(uint32_t t, uint32_t col) const { return (t * H + h) * kP + col; }
-  __device__ __forceinline__ uint32_t boff(uint32_t t, uint32_t col) const { return (t * G + g) * N + col; }
+  __device__ __forceinline__ uint32_t xoff(uint32_t t, uint32_t col) const { return t * xs + h * kP + col; }
+  __device__ __forceinline__ uint32_t boff(uint32_t t, uint32_t col) const { return t * bs + g * N + col; }
+  // dense [.., H, P] offset (out)
+  __device__ __forceinline__ uint32_t ooff(uint32_t t, uint32_t col) const { return (t * H + h) * kP + col; }
 };
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
@@ -345,13 +352,14 @@ __device__ __forceinline__ uint32_t dt_token(int Q, uint32_t tid) {
 }
 __device__ __forceinline__ uint32_t dt_token(int Q) { return dt_token(Q, threadIdx.x); }
 
-__device__ __forceinline__ float load_dt(rsrc_t rdt, uint32_t H, uint32_t h, uint32_t t0, int Q,
+// raw dt of token t0 + dt_token (dt tokens dts elements apart)
+__device__ __forceinline__ float load_dt(rsrc_t rdt, uint32_t dts, uint32_t h, uint32_t t0, int Q,
                                          uint32_t tid) {
   return __uint_as_float(
-      __builtin_amdgcn_raw_buffer_load_b32(rdt, ((t0 + dt_token(Q, tid)) * H + h) * 4, 0, 0));
+      __builtin_amdgcn_raw_buffer_load_b32(rdt, ((t0 + dt_token(Q, tid)) * dts + h) * 4, 0, 0));
 }
-__device__ __forceinline__ float load_dt(rsrc_t rdt, uint32_t H, uint32_t h, uint32_t t0, int Q) {
-  return load_dt(rdt, H, h, t0, Q, threadIdx.x);
+__device__ __forceinline__ float load_dt(rsrc_t rdt, uint32_t dts, uint32_t h, uint32_t t0, int Q) {
+  return load_dt(rdt, dts, h, t0, Q, threadIdx.x);
 }
 
 template <int Q>
@@ -594,12 +602,12 @@ struct ZRaw {
 };
 
 template <int T>
-__device__ __forceinline__ void load_z(rsrc_t rz, bool bf16, uint32_t H, uint32_t h, uint32_t tb,
+__device__ __forceinline__ void load_z(rsrc_t rz, bool bf16, uint32_t zs, uint32_t h, uint32_t tb,
                                        ZRaw<T> &r) {
 #pragma unroll
   for (int k = 0; k < ZRaw<T>::K; ++k) {
     const int u = threadIdx.x + T * k;
-    const uint32_t off = ((tb + u / 8) * H + h) * kP + 8 * (u % 8);
+    const uint32_t off = (tb + u / 8) * zs + h * kP + 8 * (u % 8);
     if (bf16) {
       r.lo[k] = IoBF16::load8(rz, off);
     } else {
@@ -794,7 +802,7 @@ __global__ __launch_bounds__(256 * HW) void ssd_group_state_kernel(Params p) {
   const uint32_t tg = (uint32_t)(c_begin * Q);
   auto tok = [&](int i) { return tg + (uint32_t)(kJB * (i < nblk ? i : nblk - 1)); };
 
-  const rsrc_t rdt = make_rsrc(p.dt + rs.start * p.H, (uint32_t)(rs.len * p.H * 4));
+  const rsrc_t rdt = make_rsrc(p.dt + rs.start * p.dts, (uint32_t)(rs.len * p.dts * 4));
   const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
 
   // one block in registers: this thread's B units and its head's x unit
@@ -825,7 +833,7 @@ __global__ __launch_bounds__(256 * HW) void ssd_group_state_kernel(Params p) {
     // next chunk's LDS scalars when the block is staged, so its wait is the
     // block's own
     r.dt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-        rdt, ((tg + (uint32_t)(kJB * (i + NB)) + dt_token(kJB, tid)) * sv.H + sv.h) * 4, 0, 0));
+        rdt, ((tg + (uint32_t)(kJB * (i + NB)) + dt_token(kJB, tid)) * sv.dts + sv.h) * 4, 0, 0));
   };
   auto store = [&](const Raw &r, int jb, const ChunkLds<Q> &cl) {
 #pragma unroll
@@ -860,7 +868,7 @@ __global__ __launch_bounds__(256 * HW) void ssd_group_state_kernel(Params p) {
     }
   };
 
-  stage_dt<Q>(load_dt(rdt, sv.H, sv.h, tg, Q, tid), clb[hh][c_begin & 1], tid);
+  stage_dt<Q>(load_dt(rdt, sv.dts, sv.h, tg, Q, tid), clb[hh][c_begin & 1], tid);
   // (scheduling barriers keep every buffer's loads in the same issue order
   // before and inside the loop, so the compiler can count them exactly)
   Raw nx0, nx1;
@@ -993,8 +1001,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   const uint64_t lhp = (uint64_t)rs.len * p.H * kP, ohp = (uint64_t)rs.start * p.H * kP;
   const int osz = p.out_bf16 ? 2 : 4, zsz = p.z_bf16 ? 2 : 4;
   const rsrc_t rout = make_rsrc(static_cast<char *>(p.out) + ohp * osz, (uint32_t)(lhp * osz));
-  const rsrc_t rz = make_rsrc(HAS_Z ? static_cast<const char *>(p.z) + ohp * zsz : nullptr,
-                              HAS_Z ? (uint32_t)(lhp * zsz) : 0u);
+  const rsrc_t rz = make_rsrc(HAS_Z ? static_cast<const char *>(p.z) + rs.start * p.zs * zsz : nullptr,
+                              HAS_Z ? (uint32_t)(rs.len * p.zs * zsz) : 0u);
   const bool z_bf16 = p.z_bf16 != 0;
   const float Dh = p.D ? p.D[h] : 0.f;
   const int64_t bh = b * p.H + h;
@@ -1007,9 +1015,9 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   BlockRaw<N, IO, T> nxt;
   ZRaw<T> nz;
   auto load_zb = [&](uint32_t tb) {
-    if (HAS_Z) load_z<T>(rz, z_bf16, sv.H, sv.h, tb, nz);
+    if (HAS_Z) load_z<T>(rz, z_bf16, (uint32_t)p.zs, sv.h, tb, nz);
   };
-  const rsrc_t rdt = make_rsrc(p.dt + rs.start * p.H, (uint32_t)(rs.len * p.H * 4));
+  const rsrc_t rdt = make_rsrc(p.dt + rs.start * p.dts, (uint32_t)(rs.len * p.dts * 4));
   const float a_h = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.f;
   typename IO::BC::raw8 craw[NR][KB];
   auto load_c = [&](uint32_t t0) {
@@ -1029,8 +1037,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   // initial state and the first R group aggregates, which arrive with the
   // block instead of one round trip after it.
   // dt two chunks ahead in registers, one chunk ahead in LDS.
-  const float dt0 = load_dt(rdt, sv.H, sv.h, (uint32_t)(c_begin * Q), Q);
-  float dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c_begin + 1 < c_end ? c_begin + 1 : c_begin) * Q), Q);
+  const float dt0 = load_dt(rdt, sv.dts, sv.h, (uint32_t)(c_begin * Q), Q);
+  float dtr = load_dt(rdt, sv.dts, sv.h, (uint32_t)((c_begin + 1 < c_end ? c_begin + 1 : c_begin) * Q), Q);
 
   // state entering this group: state_passing over the groups before it,
   // S = exp(Lam_grp[i]) S + S_grp[i] for i < j starting from h0 (or zero),
@@ -1102,7 +1110,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
     lds_barrier();
     // chunk c-1's readers of the other buffer passed the barrier above
     stage_dt<Q>(dtr, clb[(c + 1) & 1]);
-    dtr = load_dt(rdt, sv.H, sv.h, (uint32_t)((c + 2 < c_end ? c + 2 : c) * Q), Q);
+    dtr = load_dt(rdt, sv.dts, sv.h, (uint32_t)((c + 2 < c_end ? c + 2 : c) * Q), Q);
 
     // B operand of B.C^T and A operand of C.S^T share this layout
     frag cfr[NR][KB];
@@ -1282,7 +1290,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
             yv[pt][r] = y;
           }
         }
-        const uint32_t off0 = sv.xoff(t0 + kJB * jb + lrow, 16 * pt0 + lr);
+        const uint32_t off0 = sv.ooff(t0 + kJB * jb + lrow, 16 * pt0 + lr);
         const uint32_t rstep = sv.H * kP;  // elements between consecutive tokens
         if (p.out_bf16) {
 #pragma unroll
