@@ -43,6 +43,8 @@ from workloads import (CONV_WIDTH, NORM_EPS, WORKLOADS, Workload, conv_inputs, c
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "SSD fwd ms & tokens/s at [B,L,H,P,N,chunk,G]; % of MFMA/HBM roofline"
 NORM_METRIC = "gated RMSNorm ms & tokens/s at [B*L, H*P], G groups; % of HBM roofline"
+FUSED_METRIC = ("SSD fwd with the gated RMSNorm fused into its epilogue, ms & tokens/s at "
+                "[B,L,H,P,N,chunk,G], G norm groups; % of HBM roofline")
 CONV_METRIC = "causal conv1d ms & tokens/s at [B, D, S], width 4; % of HBM roofline"
 BWD_METRIC = "SSD bwd ms & tokens/s at [B,L,H,P,N,chunk,G] (fp32, P=N=chunk=64); % of fp32 roofline"
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published
@@ -411,6 +413,95 @@ def norm_main(args, w: Workload) -> int:
     return 0
 
 
+def fused_main(args, w: Workload) -> int:
+    """The forward with the gated RMSNorm fused into its epilogue (norm groups
+    = G, the chain's), against the same chain as two launches: the forward
+    without the gate, then the gated RMSNorm kernel over its output."""
+    import mamba_ssd_chunked_04_amd as ssd
+    dev = "cuda:0"
+    if args.mma == "auto":
+        args.mma = "bf16" if w.io_dtype == "bf16" else "f16"
+    abytes = algorithmic_bytes(w) + 4 * w.nheads * w.headdim       # + the norm weight
+    n_sets = args.sets or max(1, min(16, math.ceil(2 * 512e6 / abytes)))
+    print(f"[bench] fused norm after {w.name} {w.shape_str()} mma={args.mma} sets={n_sets}",
+          file=sys.stderr, flush=True)
+    sets = [{k: (None if v is None else v.to(dev)) for k, v in make_inputs(w).items()}]
+    for k in range(1, n_sets):
+        sets.append(gpu_input_set(w, w.seed * 1000 + k, dev))
+    g = torch.Generator().manual_seed(w.seed + 77)
+    wt = (1.0 + 0.1 * torch.randn(w.nheads * w.headdim, generator=g)).to(dev)
+    rows, dim = w.tokens, w.nheads * w.headdim
+    fused, sep = [], []
+    for d in sets:
+        kw = dict(D=d["D"], initial_states=d["initial_states"], dt_softplus=True,
+                  return_final_state=True, mma=args.mma, chunks_per_wg=args.chunks_per_wg,
+                  cu_seqlens=d.get("cu_seqlens"), max_seqlen=w.max_len if w.packed else None)
+        call, _, _, _ = ssd.prepare(d["x"], d["dt"], d["A"], d["B"], d["C"], w.chunk, z=d["z"],
+                                    norm_weight=wt, norm_eps=NORM_EPS, norm_groups=w.ngroups, **kw)
+        fused.append(call)
+        scall, out, _, _ = ssd.prepare(d["x"], d["dt"], d["A"], d["B"], d["C"], w.chunk, **kw)
+        zv = None if d["z"] is None else d["z"].view(rows, dim)
+        sep.append((scall, out.view(rows, dim), zv, torch.empty(rows, dim, device=dev)))
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+    copy_calibration(args.copy_calibration_mb, dev)
+
+    def run_sep(k):
+        scall, y, zv, nout = sep[k % n_sets]
+        scall.launch(stream)
+        ssd.rmsnorm_gated(y, zv, wt, w.ngroups, NORM_EPS, out=nout)
+
+    def timed(step, K):
+        for k in range(args.warmup):
+            step(k)
+        torch.cuda.synchronize()
+        e0, e1 = ev.create(), ev.create()
+        t0 = time.perf_counter()
+        ev.record(e0, stream)
+        for k in range(K):
+            step(k)
+        ev.record(e1, stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = ev.elapsed_ms(e0, e1) / K
+        ev.destroy(e0)
+        ev.destroy(e1)
+        return ms, wall / K
+
+    K = args.steps
+    fused_ms, fused_wall = timed(lambda k: fused[k % n_sets].launch(stream), K)
+    for c in fused:
+        c.check()                     # raises if an exchange timed out
+    sep_ms, _ = timed(run_sep, K)
+    achieved = abytes / (fused_ms * 1e-3) / 1e9
+    rec = {
+        "metric": FUSED_METRIC,
+        "value": w.tokens / fused_wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": fused_wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.mma,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} {w.shape_str()} + fused gated RMSNorm",
+                   "norm_groups": w.ngroups, "group_size": dim // w.ngroups, "eps": NORM_EPS,
+                   "z": w.has_z, "io_dtype": w.io_dtype, "input_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name, "ssd_fwd_norm"),
+                     "kernel": "ssd_fwd with norm_weight (every kernel of one call)",
+                     "kernel_ms": fused_ms, "algorithmic_bytes": abytes},
+        "separate_chain": {"kernels": "ssd_fwd without the gate, then gated_rmsnorm_kernel",
+                           "ms": sep_ms, "fused_speedup": sep_ms / fused_ms},
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def packed_cpu_baseline(w: Workload, d, budget_s: float, threads: int):
     """The fp64 packed oracle (each sequence through the recurrence) over the
     whole packed workload, repeated to about ``budget_s`` seconds."""
@@ -638,7 +729,9 @@ def main(argv=None):
     ap.add_argument("--config", default="same_device", choices=sorted(WORKLOADS) + ["page"],
                     help="workload; 'page' is the conv1d test shape of --op causal_conv1d")
     ap.add_argument("--op", default="ssd_fwd", choices=["ssd_fwd", "ssd_bwd", "rmsnorm_gated",
-                                                        "causal_conv1d"])
+                                                        "causal_conv1d", "ssd_fwd_norm"],
+                    help="ssd_fwd_norm: the forward with the gated RMSNorm fused into its "
+                         "epilogue, timed against the forward and the norm kernel in sequence")
     ap.add_argument("--mma", default="auto", choices=["auto", "f16", "bf16", "f32"],
                     help="MFMA operand precision; auto = bf16 for bf16 storage, else f16")
     ap.add_argument("--chunks-per-wg", type=int, default=0)
@@ -678,6 +771,8 @@ def main(argv=None):
     dev = "cuda:0"
     if args.op == "rmsnorm_gated":
         return norm_main(args, w)
+    if args.op == "ssd_fwd_norm":
+        return fused_main(args, w)
     if args.mma == "auto":
         args.mma = "bf16" if w.io_dtype == "bf16" else "f16"
     print(f"[bench] workload {w.name} {w.shape_str()} mma={args.mma}", file=sys.stderr, flush=True)

@@ -135,10 +135,12 @@ typedef struct ssd_desc {
                                 when the offsets break the contract above
                                 (the offsets live on the device, so this is
                                 the only place such an error can surface
-                                without a synchronisation).  The library
-                                never clears it: the caller zeroes it and
-                                reads it after synchronising.  Ignored for
-                                dense calls                               */
+                                without a synchronisation); a fused-norm
+                                call (norm_weight below, dense or packed)
+                                stores 2 into it when its exchange timed
+                                out.  The library never clears it: the
+                                caller zeroes it and reads it after
+                                synchronising                             */
   /* Token strides, in elements: the distance between consecutive tokens of
      x, of B (and C, the same), of z and of dt.  0 means the dense layout
      (H*P, G*N, H*P and H).  A larger stride reads these tensors as views of
@@ -154,6 +156,27 @@ typedef struct ssd_desc {
   int64_t bc_stride;
   int64_t z_stride;
   int64_t dt_stride;
+  /* Fused gated RMSNorm epilogue (page "ops-transformer MambaV2 算子套件",
+     §4.6 mamba2_rmsnormgated, which follows the scan in the chain of its §2):
+     with norm_weight set, each token's output y (after D and the z gate,
+     y * silu(z) when z is given) is normalised over groups of
+     H*P/norm_groups consecutive channels and scaled per channel,
+       out[t, c] = y[t, c] / sqrt(mean_{c' in group(c)} y[t, c']^2 + norm_eps)
+                   * norm_weight[c],
+     before its single store, so `out` is never written unnormalised.  A
+     group spans k = H/norm_groups heads (k <= 32, and k <= 16 for 256-token
+     chunks); when k > 1 their workgroups exchange per-token partial sums
+     through the workspace, as records tagged with a per-call epoch that the
+     workspace also holds.  That part of the workspace must be zero before
+     the first fused call on it, and again whenever the shape or plan of the
+     fused calls that use it changes (calls of one shape leave it ready for
+     the next).  A fused call whose exchange does not complete within about
+     20 ms stores 2 into *error_flag (when given) and leaves those rows of
+     `out` undefined.  ssd_fwd_noalloc keeps this part in its own
+     zero-initialised region of the scratch, which no other call touches. */
+  const float *norm_weight;  /* [H*P] fp32, or NULL (no fused norm)        */
+  float norm_eps;            /* > 0 and finite when norm_weight is set      */
+  int32_t norm_groups;       /* >= 1, H % norm_groups == 0                  */
 } ssd_desc;
 
 /* Fills `d` with defaults for the given shape: fp32 storage (x, B, C, z,
@@ -192,8 +215,12 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A,
                    const ssd_desc *d);
 
 /* Largest workspace, in bytes, that ssd_fwd_noalloc serves from its static
- * scratch (compare ssd_fwd_workspace_size against it). */
+ * scratch (compare ssd_fwd_workspace_size against it).  The first
+ * SSD_FWD_NOALLOC_SYNC_BYTES of the scratch are kept for the fused norm's
+ * exchange (256 bytes plus 8 bytes per head and token of the call), the rest
+ * for everything else the plan needs. */
 #define SSD_FWD_NOALLOC_MAX_SCRATCH ((size_t)64 << 20)
+#define SSD_FWD_NOALLOC_SYNC_BYTES ((size_t)24 << 20)
 
 /* ssd_fwd for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
@@ -208,8 +235,9 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A,
  * call); SSD_ERR_INVALID_ARG when the stream is not on the current device;
  * SSD_ERR_LAUNCH when the runtime cannot give the scratch address.  Every
  * call on one GPU shares its scratch, so calls that overlap on one GPU (on
- * different streams) race and must be serialised by the caller; nothing in
- * the scratch needs to start at zero. */
+ * different streams) race and must be serialised by the caller.  Only the
+ * fused norm's region needs a known start: it is zero when the library
+ * loads and holds nothing but tagged records and the epoch afterwards. */
 ssd_status ssd_fwd_noalloc(const void *x, const float *dt, const float *A,
                            const void *B, const void *C, const float *D,
                            int64_t chunk, int dt_softplus, int return_final_state,
@@ -326,7 +354,7 @@ const char *ssd_status_str(int status);
 /* ABI version of this header (bumped on any incompatible change). */
 int ssd_abi_version(void);
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

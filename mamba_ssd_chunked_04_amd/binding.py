@@ -22,8 +22,9 @@ EXPORTED_SYMBOLS = ("ssd_desc_init", "ssd_fwd_workspace_size", "ssd_fwd_plan", "
                     "ssd_fwd_noalloc", "ssd_bwd_workspace_size", "ssd_bwd", "ssd_rmsnorm_gated",
                     "ssd_causal_conv1d", "ssd_causal_conv1d_tokmajor", "ssd_status_str",
                     "ssd_abi_version")
-# include/ssd_mi355x.h: SSD_FWD_NOALLOC_MAX_SCRATCH
+# include/ssd_mi355x.h: SSD_FWD_NOALLOC_MAX_SCRATCH, SSD_FWD_NOALLOC_SYNC_BYTES
 NOALLOC_MAX_SCRATCH = 64 << 20
+NOALLOC_SYNC_BYTES = 24 << 20
 
 
 class SsdDesc(ctypes.Structure):
@@ -42,6 +43,8 @@ class SsdDesc(ctypes.Structure):
         ("error_flag", ctypes.c_void_p),
         ("x_stride", ctypes.c_int64), ("bc_stride", ctypes.c_int64),
         ("z_stride", ctypes.c_int64), ("dt_stride", ctypes.c_int64),
+        ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+        ("norm_groups", ctypes.c_int32),
     ]
 
 
@@ -174,7 +177,7 @@ class SsdCall:
         self._args = args
         self.desc = desc
         self._keep = keep        # tensors whose storage the pointers refer to
-        self.error_flag = error_flag   # packed calls: the device flag the kernels set
+        self.error_flag = error_flag   # packed or fused-norm calls: the device flag the kernels set
         self.noalloc = noalloc   # launch through ssd_fwd_noalloc
 
     def launch(self, stream: int) -> None:
@@ -196,25 +199,44 @@ class SsdCall:
         _raise_for(st, "ssd_fwd_noalloc")
 
     def check(self) -> None:
-        """Packed calls: synchronise and raise ValueError if any launch of this
-        call found cu_seqlens breaking its contract (a sequence longer than
-        max_seqlen, decreasing offsets or one past the packed tokens); the
-        flag is then cleared.  A no-op for dense calls."""
+        """Packed or fused-norm calls: synchronise and raise if any launch of
+        this call set the device flag -- ValueError when cu_seqlens broke its
+        contract (a sequence longer than max_seqlen, decreasing offsets or one
+        past the packed tokens), SsdError when the fused norm's exchange
+        between workgroups timed out (the workspace's synchronisation words
+        are then zeroed again here); the flag is then cleared.  A no-op for
+        other calls."""
         if self.error_flag is None:
             return
-        if int(self.error_flag.item()) != 0:
-            self.error_flag.zero_()
-            raise ValueError("ssd_fwd: cu_seqlens breaks the call's contract (a sequence longer "
-                             "than max_seqlen, decreasing offsets or an offset past the packed "
-                             "tokens); the results of those sequences are undefined")
+        v = int(self.error_flag.item())
+        if v == 0:
+            return
+        self.error_flag.zero_()
+        if v == 2:
+            ws = self._keep[11]
+            if ws is not None:
+                ws.zero_()
+            raise SsdError(SSD_ERR_LAUNCH, "ssd_fwd: the fused norm's exchange between "
+                           "workgroups timed out; `out` is undefined")
+        raise ValueError("ssd_fwd: cu_seqlens breaks the call's contract (a sequence longer "
+                         "than max_seqlen, decreasing offsets or an offset past the packed "
+                         "tokens); the results of those sequences are undefined")
 
 
 def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initial_states=None,
             dt_softplus: bool = False, dt_limit: Tuple[float, float] = (0.0, math.inf),
             return_final_state: bool = False, mma: str = "f16", out_dtype=None,
             chunks_per_wg: int = 0, out=None, final_state=None, workspace=None,
-            cu_seqlens=None, max_seqlen: Optional[int] = None, noalloc: bool = False):
+            cu_seqlens=None, max_seqlen: Optional[int] = None, noalloc: bool = False,
+            norm_weight=None, norm_eps: float = 1e-5, norm_groups: Optional[int] = None):
     """Validate torch tensors, allocate outputs/workspace, and build an SsdCall.
+
+    With ``norm_weight`` ([H*P] float32) the gated RMSNorm that follows the
+    scan is fused into its epilogue: out = rmsnorm(y) * norm_weight over
+    ``norm_groups`` groups of each token's H*P channels (default: G), where y
+    already carries D and the z gate.  The workspace is then allocated zeroed
+    (it holds the exchange's synchronisation words); a caller-given one must
+    be zeroed before its first fused call.
 
     With ``noalloc`` no workspace is allocated and the call launches through
     ``ssd_fwd_noalloc`` (the library's static scratch; ValueError from the
@@ -299,11 +321,20 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
         final_state = torch.empty(nrows, H, P, N, device=dev, dtype=torch.float32)
     desc = make_desc(nrows, row_len, H, P, N, G)
     error_flag = None
+    if cu_seqlens is not None or norm_weight is not None:
+        error_flag = torch.zeros(1, device=dev, dtype=torch.int32)
+        desc.error_flag = error_flag.data_ptr()
     if cu_seqlens is not None:
         desc.cu_seqlens = cu_seqlens.data_ptr()
         desc.packed_tokens = L
-        error_flag = torch.zeros(1, device=dev, dtype=torch.int32)
-        desc.error_flag = error_flag.data_ptr()
+    if norm_weight is not None:
+        if (not isinstance(norm_weight, torch.Tensor) or norm_weight.device != dev
+                or norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (H * P,)
+                or not norm_weight.is_contiguous()):
+            raise ValueError("norm_weight must be a contiguous float32 [H*P] tensor on the GPU of x")
+        desc.norm_weight = norm_weight.data_ptr()
+        desc.norm_eps = float(norm_eps)
+        desc.norm_groups = int(G if norm_groups is None else norm_groups)
     desc.x_dtype = _dtype_code(x.dtype)
     desc.bc_dtype = _dtype_code(B.dtype)
     desc.z_dtype = _dtype_code(z.dtype) if z is not None else SSD_F32
@@ -318,14 +349,15 @@ def prepare(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     desc.bc_stride = strides["B"] or strides["C"]
     nbytes = workspace_size(desc, chunk_size)
     if nbytes > 0 and workspace is None and not noalloc:
-        workspace = torch.empty(nbytes, device=dev, dtype=torch.uint8)
+        alloc = torch.zeros if norm_weight is not None else torch.empty
+        workspace = alloc(nbytes, device=dev, dtype=torch.uint8)
     if workspace is not None:
         desc.workspace, desc.workspace_bytes = workspace.data_ptr(), workspace.numel()
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk_size),
             int(bool(dt_softplus)), int(bool(return_final_state)), _ptr(out),
             _ptr(final_state) if return_final_state else None)
     keep = (x, dt, A, B, C, D, z, dt_bias, initial_states, out, final_state, workspace, cu_seqlens,
-            error_flag)
+            error_flag, norm_weight)
     return (SsdCall(args, desc, keep, error_flag, noalloc=noalloc), out,
             (final_state if return_final_state else None), workspace)
 
@@ -334,7 +366,8 @@ def ssd_fwd(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
             dt_softplus: bool = False, dt_limit: Tuple[float, float] = (0.0, math.inf),
             return_final_state: bool = False, mma: str = "f16", out_dtype=None,
             chunks_per_wg: int = 0, cu_seqlens=None, max_seqlen: Optional[int] = None,
-            check_offsets: bool = True, noalloc: bool = False):
+            check_offsets: bool = True, noalloc: bool = False, norm_weight=None,
+            norm_eps: float = 1e-5, norm_groups: Optional[int] = None):
     """SSD chunked forward on the current torch stream.
 
     Returns ``out`` or ``(out, final_state)`` when ``return_final_state``.
@@ -346,17 +379,22 @@ def ssd_fwd(x, dt, A, B, C, chunk_size: int, D=None, z=None, dt_bias=None, initi
     reports such offsets; ``prepare`` and ``call.check()`` give control over
     when the check runs).  ``noalloc`` runs it through ``ssd_fwd_noalloc``
     (no workspace; the outputs are still allocated here unless the caller
-    uses ``prepare`` with its own).
+    uses ``prepare`` with its own).  ``norm_weight`` fuses the gated RMSNorm
+    into the epilogue (see ``prepare``); ``check_offsets`` then also
+    synchronises to report a timed-out exchange.
     """
     import torch
     call, out, fin, _ws = prepare(x, dt, A, B, C, chunk_size, D=D, z=z, dt_bias=dt_bias,
                                   initial_states=initial_states, dt_softplus=dt_softplus,
                                   dt_limit=dt_limit, return_final_state=return_final_state,
                                   mma=mma, out_dtype=out_dtype, chunks_per_wg=chunks_per_wg,
-                                  cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, noalloc=noalloc)
+                                  cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, noalloc=noalloc,
+                                  norm_weight=norm_weight, norm_eps=norm_eps,
+                                  norm_groups=norm_groups)
     with torch.cuda.device(x.device):
         call.launch(torch.cuda.current_stream(x.device).cuda_stream)
-        if cu_seqlens is not None and max_seqlen is not None and check_offsets:
+        if check_offsets and ((cu_seqlens is not None and max_seqlen is not None)
+                              or norm_weight is not None):
             call.check()
     return (out, fin) if return_final_state else out
 

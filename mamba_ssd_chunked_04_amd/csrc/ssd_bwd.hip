@@ -726,7 +726,8 @@ ssd_status check_bwd(const ssd_desc *d, int64_t chunk) {
     return SSD_ERR_INVALID_ARG;
   if (d->headdim != kP || d->dstate != kN || chunk != kQ) return SSD_ERR_UNSUPPORTED;
   if (d->x_dtype != SSD_F32 || d->bc_dtype != SSD_F32 || (d->z && d->z_dtype != SSD_F32) ||
-      d->cu_seqlens || d->x_stride || d->bc_stride || d->z_stride || d->dt_stride)
+      d->cu_seqlens || d->x_stride || d->bc_stride || d->z_stride || d->dt_stride ||
+      d->norm_weight)
     return SSD_ERR_UNSUPPORTED;
   // 32-bit byte offsets within one batch row, 32-bit grid
   if (d->seqlen * d->nheads * kP * 4 >= ((int64_t)1 << 31) || d->batch * d->nheads >= ((int64_t)1 << 31))

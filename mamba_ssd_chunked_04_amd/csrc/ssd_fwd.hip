@@ -62,6 +62,16 @@ ssd_status check_shape(const ssd_desc *d, int64_t chunk) {
       d->seqlen * bs * 4 >= row_limit || d->seqlen * zs * 4 >= row_limit ||
       d->seqlen * dts * 4 >= row_limit)
     return SSD_ERR_UNSUPPORTED;
+  if (d->norm_weight) {
+    // fused norm: groups of k = H / norm_groups heads, whose workgroups must
+    // all be resident at once (k well below the workgroups of one XCD)
+    if (d->norm_groups < 1 || d->nheads % d->norm_groups != 0) return SSD_ERR_INVALID_ARG;
+    if (!(d->norm_eps > 0.f) || !(d->norm_eps < INFINITY)) return SSD_ERR_INVALID_ARG;
+    const int64_t k = d->nheads / d->norm_groups;
+    if (k > (chunk == 256 ? 16 : 32)) return SSD_ERR_UNSUPPORTED;
+    // one chunk's exchange record is addressed with 32-bit byte offsets
+    if (d->nheads * chunk * 4 >= row_limit) return SSD_ERR_UNSUPPORTED;
+  }
   return SSD_OK;
 }
 
@@ -100,6 +110,13 @@ Plan make_plan(const ssd_desc *d, int64_t chunk) {
   pl.state_bytes = align_up((size_t)slots * (size_t)(d->headdim * d->dstate) * sizeof(float));
   pl.lam_bytes = align_up((size_t)slots * sizeof(float));
   if (slots == 0) pl.state_bytes = pl.lam_bytes = 0;
+  pl.sync_bytes = 0;
+  if (d->norm_weight && d->nheads / d->norm_groups > 1) {
+    // the epoch and the count of finished workgroups, then one 64-bit
+    // record (partial sum, tag) per head and token of every chunk
+    pl.sync_bytes =
+        kAlign + align_up((size_t)(d->batch * pl.nc * d->nheads * chunk) * sizeof(uint64_t));
+  }
   return pl;
 }
 
@@ -109,7 +126,7 @@ bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 ssd_status fwd_impl(const void *x, const float *dt, const float *A, const void *B, const void *C,
                     const float *D, int64_t chunk, int dt_softplus, int return_final_state,
                     void *out, float *final_state, void *stream, const ssd_desc *d, void *ws,
-                    size_t ws_bytes) {
+                    size_t ws_bytes, void *sync) {
   const ssd_status st = check_shape(d, chunk);
   if (st != SSD_OK) return st;
   if (!x || !dt || !A || !B || !C || !out) return SSD_ERR_INVALID_ARG;
@@ -120,9 +137,13 @@ ssd_status fwd_impl(const void *x, const float *dt, const float *A, const void *
       (return_final_state && !aligned16(final_state)) ||
       ((uintptr_t)d->cu_seqlens & 3u) != 0 || ((uintptr_t)d->error_flag & 3u) != 0)
     return SSD_ERR_INVALID_ARG;
+  if (d->norm_weight && ((uintptr_t)d->norm_weight & 3u) != 0) return SSD_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, chunk);
-  const size_t need = pl.total();
+  // the counters sit at `sync` (the workspace's start, or the noalloc
+  // scratch's own region) and everything else at `ws`
+  const size_t need = sync == ws ? pl.total() : pl.data_bytes();
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return SSD_ERR_WORKSPACE;
+  if (pl.sync_bytes && (!sync || ((uintptr_t)sync & 15u) != 0)) return SSD_ERR_WORKSPACE;
 
   Params prm;
   memset(&prm, 0, sizeof(prm));
@@ -137,11 +158,18 @@ ssd_status fwd_impl(const void *x, const float *dt, const float *A, const void *
   prm.h0 = d->initial_state;
   prm.out = out;
   prm.final_state = final_state;
-  char *wsc = static_cast<char *>(ws);
+  char *wsc = static_cast<char *>(ws) + (sync == ws ? pl.sync_bytes : 0);
+  prm.norm_sync = pl.sync_bytes ? static_cast<uint64_t *>(sync) : nullptr;
+  prm.norm_rec = pl.sync_bytes ? reinterpret_cast<uint64_t *>(static_cast<char *>(sync) + kAlign)
+                               : nullptr;
   prm.grp_state = pl.state_bytes ? reinterpret_cast<float *>(wsc) : nullptr;
   prm.grp_lam = pl.lam_bytes ? reinterpret_cast<float *>(wsc + pl.state_bytes) : nullptr;
+  prm.norm_w = d->norm_weight;
+  prm.norm_eps = d->norm_eps;
+  prm.norm_k = d->norm_weight ? (int)(d->nheads / d->norm_groups) : 1;
+  prm.nchk_row = pl.nc;
   prm.cu_seqlens = d->cu_seqlens;
-  prm.error_flag = d->cu_seqlens ? d->error_flag : nullptr;
+  prm.error_flag = (d->cu_seqlens || d->norm_weight) ? d->error_flag : nullptr;
   prm.packed_tokens = d->cu_seqlens ? d->packed_tokens : 0;
   prm.xs = d->x_stride ? d->x_stride : d->nheads * d->headdim;
   prm.bs = d->bc_stride ? d->bc_stride : d->ngroups * d->dstate;
@@ -177,6 +205,7 @@ ssd_status fwd_impl(const void *x, const float *dt, const float *A, const void *
 // code `scratch` only names the symbol; its device address on each GPU comes
 // from hipGetSymbolAddress, taken once per device and kept in scratch_ptr.
 constexpr size_t kScratchBytes = SSD_FWD_NOALLOC_MAX_SCRATCH;
+constexpr size_t kSyncBytes = SSD_FWD_NOALLOC_SYNC_BYTES;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -247,7 +276,7 @@ ssd_status ssd_fwd(const void *x, const float *dt, const float *A, const void *B
                    void *out, float *final_state, void *stream, const ssd_desc *d) {
   if (!d) return SSD_ERR_INVALID_ARG;
   return fwd_impl(x, dt, A, B, C, D, chunk, dt_softplus, return_final_state, out, final_state,
-                  stream, d, d->workspace, d->workspace_bytes);
+                  stream, d, d->workspace, d->workspace_bytes, d->workspace);
 }
 
 ssd_status ssd_fwd_noalloc(const void *x, const float *dt, const float *A, const void *B,
@@ -258,7 +287,8 @@ ssd_status ssd_fwd_noalloc(const void *x, const float *dt, const float *A, const
   const ssd_status st = check_shape(d, chunk);
   if (st != SSD_OK) return st;
   const Plan pl = make_plan(d, chunk);
-  if (pl.total() > kScratchBytes) return SSD_ERR_WORKSPACE;
+  if (pl.sync_bytes > kSyncBytes || pl.data_bytes() > kScratchBytes - kSyncBytes)
+    return SSD_ERR_WORKSPACE;
   if (!x || !dt || !A || !B || !C || !out) return SSD_ERR_INVALID_ARG;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_LAUNCH;
@@ -266,10 +296,12 @@ ssd_status ssd_fwd_noalloc(const void *x, const float *dt, const float *A, const
   if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
     return SSD_ERR_INVALID_ARG;
   if ((int)sdev != dev) return SSD_ERR_INVALID_ARG;  // the scratch address is per device
-  void *ws = pl.total() > 0 ? scratch_ptr(dev) : nullptr;
-  if (pl.total() > 0 && !ws) return SSD_ERR_LAUNCH;
+  char *base = pl.total() > 0 ? static_cast<char *>(scratch_ptr(dev)) : nullptr;
+  if (pl.total() > 0 && !base) return SSD_ERR_LAUNCH;
+  // the first kSyncBytes hold the fused norm's exchange (zero at load, then
+  // only its epoch and tagged records), the rest the plan's other parts
   return fwd_impl(x, dt, A, B, C, D, chunk, dt_softplus, return_final_state, out, final_state,
-                  stream, d, ws, kScratchBytes);
+                  stream, d, base ? base + kSyncBytes : nullptr, kScratchBytes - kSyncBytes, base);
 }
 
 const char *ssd_status_str(int status) {

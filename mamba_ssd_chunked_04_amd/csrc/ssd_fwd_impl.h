@@ -215,6 +215,16 @@ struct Params {
   float dt_min, dt_max;
   int dt_softplus, z_bf16, out_bf16, ret_final;
   int chained;  // grp_state holds entering states (the passing pass ran)
+  // fused gated RMSNorm epilogue (norm_w != NULL): groups of norm_k heads,
+  // exchanged per chunk through norm_rec [B][nchk_row][H][Q] (per-token
+  // partial sums of squares, each with the call's tag) and norm_sync (the
+  // epoch the tags derive from, and the count of finished workgroups)
+  const float *norm_w;
+  uint64_t *norm_rec;
+  uint64_t *norm_sync;
+  int64_t nchk_row;
+  float norm_eps;
+  int norm_k;
 };
 
 // Workgroup id -> (b, h, chunk group).  Tiles are ordered (b, group, g, head
@@ -595,6 +605,7 @@ __device__ __forceinline__ void store_block(const BlockRaw<N, IO, T> &r, int jb,
 // The z gate of one 64-token block, staged like x so each row's epilogue
 // finds it in LDS: unit u holds row u/8, columns 8 (u%8) .. +8.
 typedef unsigned int u32x4v __attribute__((vector_size(16)));
+typedef unsigned int u32x2v __attribute__((vector_size(8)));
 template <int T>
 struct ZRaw {
   static constexpr int K = 512 / T;
@@ -956,12 +967,99 @@ __global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------- fused norm
+// The gated RMSNorm that follows the scan (page "ops-transformer MambaV2
+// 算子套件", §4.6, in the chain order of its §2) normalises each token over
+// groups of k heads.  Every head is a different workgroup, so the k
+// workgroups of a group exchange, once per chunk, the per-token partial
+// sums of squares of their 64 channels.  Each partial is one 64-bit record:
+// the fp32 sum in the low half and the call's tag in the high half, stored
+// with one device-scope (sc1, written through its XCD's L2) store, so a
+// reader that sees the tag sees the sum.  A wave that needs its rows' sums
+// loads the k members' records with device-scope loads and loads again
+// until every tag is this call's.  The tag is one more than an epoch word
+// that the last workgroup of every launch advances, so records left by an
+// earlier call (or by an earlier replay of a captured graph) never match.
+//
+// The k workgroups of a group are consecutive tiles, which are consecutive
+// in the dispatch order of one XCD (decode_tile), so a waiting wave's
+// partners are already resident or are dispatched once earlier, complete
+// groups finish (at most one group per XCD is partly dispatched, and k is
+// far below the workgroups an XCD holds).  The wait is still bounded (20 ms
+// of the 100 MHz real-time counter): on a time-out *error_flag is set to 2
+// and those rows come out undefined, but the kernel ends.
+constexpr int kSc1 = 16;                    // cache-policy bit of buffer ops: device scope
+constexpr uint64_t kNormTicks = 2000000;    // 20 ms
+
+// Sum over the 16 lanes of a quarter-wave (lanes 16q .. 16q+15); every lane
+// ends with the same value (each butterfly stage adds the same two terms).
+__device__ __forceinline__ f32x4 quarter_sum(f32x4 v) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] += __shfl_xor(v[r], m, 64);
+  return v;
+}
+
+// This launch's tag: the epoch the previous launch left, plus one.
+__device__ __forceinline__ uint32_t norm_tag(const Params &p) {
+  return (uint32_t)__hip_atomic_load(p.norm_sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+}
+
+// The end of a workgroup (every one, early exits included): the last of the
+// launch zeroes the count and advances the epoch for the next launch.  Every
+// workgroup has read its tag and all its records before it counts itself.
+__device__ __forceinline__ void norm_done(const Params &p) {
+  if (threadIdx.x != 0) return;
+  const uint64_t old =
+      __hip_atomic_fetch_add(p.norm_sync + 1, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old + 1 == (uint64_t)gridDim.x) {
+    __hip_atomic_store(p.norm_sync + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(p.norm_sync, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The records of one member (head hm) for four consecutive rows of a chunk.
+struct NormRec {
+  u32x4v a, b;  // rows r, r+1 and r+2, r+3: (sum bits, tag) each
+};
+__device__ __forceinline__ NormRec norm_load(rsrc_t rx, int Q, int64_t hm, int row) {
+  const uint32_t off = (uint32_t)((hm * Q + row) * 8);
+  NormRec r;
+  r.a = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, kSc1));
+  r.b = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, kSc1));
+  return r;
+}
+__device__ __forceinline__ bool norm_ready(const NormRec &r, uint32_t tag) {
+  return r.a[1] == tag && r.a[3] == tag && r.b[1] == tag && r.b[3] == tag;
+}
+// Wait until member hm's records carry `tag` (`r` holds a first load);
+// returns their four sums.
+__device__ __forceinline__ f32x4 norm_take(const Params &p, rsrc_t rx, int Q, int64_t hm, int row,
+                                           uint32_t tag, NormRec r) {
+  if (!norm_ready(r, tag)) {
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kNormTicks;
+    for (;;) {
+      __builtin_amdgcn_s_sleep(1);
+      r = norm_load(rx, Q, hm, row);
+      if (norm_ready(r, tag)) break;
+      if (__builtin_amdgcn_s_memrealtime() > t_end) {
+        if (p.error_flag)
+          __hip_atomic_store(p.error_flag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  return f32x4{__uint_as_float(r.a[0]), __uint_as_float(r.a[2]), __uint_as_float(r.b[0]),
+               __uint_as_float(r.b[2])};
+}
+
 // Main pass: chunk_scan over the chunks of one group with W waves, carrying
 // the state.  Per chunk: the inter-chunk term C.S_in^T from the carried
 // state, then per 64-token block the intra-chunk term, the block's
 // contribution to the carried state and the epilogue of the rows the block
 // completes; the next block's loads are issued before its matrix work.
-template <int Q, int N, int MM, class IO, int W, bool HAS_Z>
+template <int Q, int N, int MM, class IO, int W, bool HAS_Z, bool HAS_NORM>
 __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   constexpr int T = 64 * W;
   using E = typename Mma<MM>::T;
@@ -984,14 +1082,24 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) E sS[kP * LDN];
   __shared__ __attribute__((aligned(16))) float sZ[HAS_Z ? kJB * LDZ : 4];
   __shared__ __attribute__((aligned(16))) ChunkLds<Q> clb[2];
+  __shared__ float snw[HAS_NORM ? kP : 1];
 
+  // fused norm with an exchange: every workgroup counts itself out at its end
+  const bool nx = HAS_NORM && p.norm_k > 1;
   int64_t b, h, j;
-  if (!decode_tile(p, p.ngroups, b, h, j, true)) return;
+  if (!decode_tile(p, p.ngroups, b, h, j, true)) {
+    if (nx) norm_done(p);
+    return;
+  }
   if (p.cu_seqlens && p.error_flag && j == 0 && threadIdx.x == 0 && offsets_break_contract(p, b))
     __builtin_amdgcn_raw_buffer_store_b32(1u, make_rsrc(p.error_flag, 4u), 0, 0, 0);
   const RowSpan rs = row_span(p, b);
   const int64_t ng_row = row_groups(p, rs.len), nc_row = row_chunks(p, rs.len);
-  if (j >= ng_row) return;  // past the end of a shorter packed sequence
+  if (j >= ng_row) {  // past the end of a shorter packed sequence
+    if (nx) norm_done(p);
+    return;
+  }
+  const uint32_t ntag = nx ? norm_tag(p) : 0u;
   // the wave index is uniform: read it into a scalar so per-wave tests branch
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lq = lane >> 4;
@@ -1005,6 +1113,11 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
                               HAS_Z ? (uint32_t)(rs.len * p.zs * zsz) : 0u);
   const bool z_bf16 = p.z_bf16 != 0;
   const float Dh = p.D ? p.D[h] : 0.f;
+  // fused norm: the head's 64 channel weights, staged in LDS (read after
+  // the prologue's barrier)
+  if constexpr (HAS_NORM) {
+    if (w == 0) snw[lane] = p.norm_w[h * kP + lane];  // (a wave-uniform branch)
+  }
   const int64_t bh = b * p.H + h;
   const int64_t c_begin = j * p.cpg;
   const int64_t c_end = (c_begin + p.cpg < nc_row) ? c_begin + p.cpg : nc_row;
@@ -1099,6 +1212,90 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   }
   lds_barrier();  // the first chunk's staged dt
 
+  // output accumulators of this wave's row tiles (with the fused norm they
+  // hold the chunk's gated y until its exchange ends at the chunk's end)
+  f32x4 yacc[NR][PT];
+  // the epilogue's store of four rows of a tile from token `tok` of the row
+  // (rows past the sequence end are dropped by the buffer range check)
+  const uint32_t rstep = sv.H * kP;  // elements between consecutive tokens of out
+  auto store_rows = [&](uint32_t tok, const f32x4 (&yv)[PT]) {
+    const uint32_t off0 = sv.ooff(tok, 16 * pt0 + lr);
+    if (p.out_bf16) {
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(yv[pt][r]), rout,
+                                                (off0 + r * rstep + 16 * pt) * 2, 0, 0);
+    } else {
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[pt][r]), rout,
+                                                (off0 + r * rstep + 16 * pt) * 4, 0, 0);
+    }
+  };
+  // fused norm: chunk cc's exchange record (partial sums of squares per
+  // head and token), and the end of its exchange -- the wait, then every
+  // tile of the chunk (its gated y in the accumulators) normalised and
+  // stored; nbc = the chunk's 64-token blocks
+  auto norm_record = [&](int64_t cc) {
+    return make_rsrc(nx ? p.norm_rec + ((b * p.nchk_row + cc) * p.H) * Q : nullptr,
+                     nx ? (uint32_t)(p.H * Q * 8) : 0u);
+  };
+  const int64_t h0n = h - h % p.norm_k;  // the norm group's first head
+  // the sums over the group's members for rows crow .. crow+3 of chunk cc
+  // (lane lr takes members lr, lr+16; then the quarter-wave adds them up)
+  auto norm_sums = [&](int64_t cc, int crow) {
+    const rsrc_t rxc = norm_record(cc);
+    f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = lr; m < p.norm_k; m += 16)
+      tot += norm_take(p, rxc, Q, h0n + m, crow, ntag, norm_load(rxc, Q, h0n + m, crow));
+    return quarter_sum(tot);
+  };
+  auto norm_scale_store = [&](int64_t cc, int crow, f32x4 tot, f32x4 (&yv)[PT]) {
+    const float inv_n = 1.f / (float)(p.norm_k * kP);
+    float rstd[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rstd[r] = __builtin_amdgcn_rsqf(tot[r] * inv_n + p.norm_eps);
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+      const float wc = snw[16 * (pt0 + pt) + lr];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yv[pt][r] *= rstd[r] * wc;
+    }
+    store_rows((uint32_t)(cc * Q + crow), yv);
+  };
+  auto own_sums = [&](const f32x4 (&yv)[PT]) {
+    f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tot[r] += yv[pt][r] * yv[pt][r];
+    return quarter_sum(tot);
+  };
+  // every tile of chunk cc (its gated y in the accumulators) normalised and
+  // stored; nbc = the chunk's 64-token blocks
+  auto norm_finish = [&](int64_t cc, int nbc) {
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int row0 = 16 * RS::tile(k, w);
+      if ((row0 >> 6) >= nbc) continue;  // past a ragged chunk's last block
+      const int crow = row0 + 4 * lq;    // row within the chunk, + r
+      const f32x4 tot = nx ? norm_sums(cc, crow) : own_sums(yacc[k]);
+      norm_scale_store(cc, crow, tot, yacc[k]);
+    }
+  };
+  // 64-token chunks (one row tile per wave) have the registers to hold a
+  // chunk's gated y for a whole chunk: their exchange arrives after the next
+  // chunk's first staging (when the partials' stores are long complete) and
+  // ends after that chunk's products, both off the critical path
+  constexpr bool kDefer = HAS_NORM && NR == 1;
+  f32x4 ydef[PT];  // (unused, and dropped by the compiler, unless kDefer)
+  int64_t pend_c = -1;  // chunk whose normalisation is pending (kDefer)
+  const int drow = 16 * RS::tile(0, w) + 4 * lq;  // kDefer: the tile's rows in a chunk
+
   for (int64_t c = c_begin; c < c_end; ++c) {
     const uint32_t t0 = (uint32_t)(c * Q);
     const int Qc = qc_of(c);
@@ -1122,7 +1319,6 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
         for (int s = 0; s < 8; ++s) cfr[k][kb][s] = (E)IO::BC::cvt8(craw[k][kb], s);
 
     // inter-chunk term: Y = diag(exp(Lam)) C S_in^T
-    f32x4 yacc[NR][PT];
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       const int row0 = 16 * RS::tile(k, w);
@@ -1149,11 +1345,32 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
       for (int t = 0; t < NN; ++t) sacc[t] *= dec;
     }
 
+    // the epilogue's pieces: a tile's y + D x with x from the staged block,
+    // times the z gate from the staged z; the store of four rows of a tile
+    // (rows past the sequence end are dropped by the buffer range check)
+    auto gated_y = [&](int k, int lrow, f32x4 (&yv)[PT]) {
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        const int col = 16 * (pt0 + pt) + lr;
+        const quad xq = *reinterpret_cast<const quad *>(&sXT[col * LDJ + lrow]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float y = yacc[k][pt][r] + Dh * (float)xq[r];
+          if (HAS_Z) {
+            const float zz = sZ[(lrow + r) * LDZ + col];
+            y *= zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz));
+          }
+          yv[pt][r] = y;
+        }
+      }
+    };
+    const rsrc_t rxn = norm_record(c);
     const int nb = nblocks(Qc);
     for (int jb = 0; jb < nb; ++jb) {
       lds_barrier();
       store_block<N, MM, IO, T, true>(nxt, jb, cl.w, sB, sBT, sXT);
       if (HAS_Z) store_z<T>(nz, z_bf16, sZ);
+      const bool def_now = kDefer && jb == 0 && pend_c >= 0;  // the pending chunk's turn
       lds_barrier();
       {
         // next block: the chunk's next one, else the next chunk's first, else
@@ -1266,48 +1483,62 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
       // chunk_state contribution of this block to the carried state
       state_block_mma<N, MM, W>(sXT, sBT, sacc);
 
+
       // epilogue of the row tiles that lie in this block (their sums are
       // complete): + D x with x from the staged block, the z gate from the
       // staged z, store (rows past the sequence end are dropped by the buffer
       // range check)
+      if constexpr (!HAS_NORM) {
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        const int row0 = 16 * RS::tile(k, w);
-        if ((row0 >> 6) != jb) continue;
-        const int lrow = row0 - kJB * jb + 4 * lq;  // row within the block, + r
-        f32x4 yv[PT];
+        for (int k = 0; k < NR; ++k) {
+          const int row0 = 16 * RS::tile(k, w);
+          if ((row0 >> 6) != jb) continue;
+          const int lrow = row0 - kJB * jb + 4 * lq;  // row within the block, + r
+          f32x4 yv[PT];
+          gated_y(k, lrow, yv);
+          store_rows(t0 + kJB * jb + lrow, yv);
+        }
+      } else {
+        // fused gated RMSNorm: the gated y of the tile this wave completes
+        // in this block (the row splits give a wave at most one per block)
+        // replaces its accumulator until the chunk's exchange; its per-row
+        // sums of squares over the head's 64 channels (this lane's PT
+        // columns, then the 16 lanes that hold the same four rows) go to
+        // the chunk's exchange record
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          const int col = 16 * (pt0 + pt) + lr;
-          const quad xq = *reinterpret_cast<const quad *>(&sXT[col * LDJ + lrow]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float y = yacc[k][pt][r] + Dh * (float)xq[r];
-            if (HAS_Z) {
-              const float zz = sZ[(lrow + r) * LDZ + col];
-              y *= zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz));
+        for (int k = 0; k < NR; ++k) {
+          const int row0 = 16 * RS::tile(k, w);
+          if ((row0 >> 6) != jb) continue;
+          const int lrow = row0 - kJB * jb + 4 * lq;
+          gated_y(k, lrow, yacc[k]);
+          if (nx) {
+            // lane r < 4 of each quarter-wave stores row r's record
+            const f32x4 ss = own_sums(yacc[k]);
+            if (lr < 4) {
+              const float v = lr == 0 ? ss[0] : lr == 1 ? ss[1] : lr == 2 ? ss[2] : ss[3];
+              const u32x2v rec = {__float_as_uint(v), ntag};
+              __builtin_amdgcn_raw_buffer_store_b64(
+                  __builtin_bit_cast(u32x2v, rec), rxn,
+                  (uint32_t)((h * Q + row0 + 4 * lq + lr) * 8), 0, kSc1);
             }
-            yv[pt][r] = y;
           }
         }
-        const uint32_t off0 = sv.ooff(t0 + kJB * jb + lrow, 16 * pt0 + lr);
-        const uint32_t rstep = sv.H * kP;  // elements between consecutive tokens
-        if (p.out_bf16) {
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(yv[pt][r]), rout,
-                                                    (off0 + r * rstep + 16 * pt) * 2, 0, 0);
-        } else {
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[pt][r]), rout,
-                                                    (off0 + r * rstep + 16 * pt) * 4, 0, 0);
+        if constexpr (kDefer) {
+          if (def_now) {
+            const f32x4 tot = nx ? norm_sums(pend_c, drow) : own_sums(ydef);
+            norm_scale_store(pend_c, drow, tot, ydef);
+          }
         }
       }
+    }
+
+    if constexpr (kDefer) {
+      // this chunk's gated y waits in ydef for its exchange
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) ydef[pt] = yacc[0][pt];
+      pend_c = c;
+    } else if constexpr (HAS_NORM) {
+      norm_finish(c, nb);  // the chunk's exchange ends here
     }
 
     // the state entering the next chunk, as the C.S^T operand (all waves
@@ -1318,6 +1549,13 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
       for (int r = 0; r < 4; ++r) sS[SS::row(r) * LDN + SS::col(t)] = (E)sacc[t][r];
   }
 
+  if constexpr (kDefer) {
+    if (pend_c >= 0) {
+      const f32x4 tot = nx ? norm_sums(pend_c, drow) : own_sums(ydef);
+      norm_scale_store(pend_c, drow, tot, ydef);
+    }
+  }
+
   if (p.ret_final && j == ng_row - 1) {
     float *dst = p.final_state + bh * (int64_t)(kP * N);
 #pragma unroll
@@ -1325,6 +1563,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[SS::row(r) * N + SS::col(t)] = sacc[t][r];
   }
+  if (nx) norm_done(p);
 }
 
 
@@ -1339,8 +1578,11 @@ constexpr int64_t kFoldGroups = 8;
 // group states and group decays.
 struct Plan {
   int64_t nc, cpg, ngroups;
+  size_t sync_bytes;       // fused norm: epoch, finish count and the tagged partial sums
   size_t state_bytes, lam_bytes;
-  size_t total() const { return state_bytes + lam_bytes; }
+  // everything after the norm's part, which ssd_fwd_noalloc keeps apart
+  size_t data_bytes() const { return state_bytes + lam_bytes; }
+  size_t total() const { return sync_bytes + data_bytes(); }
 };
 
 
@@ -1379,12 +1621,21 @@ ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, con
   // 4-wave workgroups (two per CU) for chunks of 64 and 128 tokens; 8 waves
   // for 256-token chunks, whose row tiles would not fit 4 waves' registers
   constexpr int W = main_waves<Q>();
-  if (prm.z)
-    hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, MM, IO, W, true>), dim3((unsigned)g2),
-                       dim3(64 * W), 0, stream, prm);
-  else
-    hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, MM, IO, W, false>), dim3((unsigned)g2),
-                       dim3(64 * W), 0, stream, prm);
+  const dim3 grid((unsigned)g2), block(64 * W);
+  if (prm.norm_w) {
+    if (prm.z)
+      hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, MM, IO, W, true, true>), grid, block, 0,
+                         stream, prm);
+    else
+      hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, MM, IO, W, false, true>), grid, block, 0,
+                         stream, prm);
+  } else if (prm.z) {
+    hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, MM, IO, W, true, false>), grid, block, 0,
+                       stream, prm);
+  } else {
+    hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, N, MM, IO, W, false, false>), grid, block, 0,
+                       stream, prm);
+  }
   if (hipGetLastError() != hipSuccess) return SSD_ERR_LAUNCH;
   if (d->ev_main_end && hipEventRecord(static_cast<hipEvent_t>(d->ev_main_end), stream) != hipSuccess)
     return SSD_ERR_LAUNCH;

@@ -44,11 +44,11 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(bnd.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), f"{name} not exported"
-    assert lib.ssd_abi_version() == 5
+    assert lib.ssd_abi_version() == 6
 
 
 def test_desc_layout_matches_c(lib):
-    assert ctypes.sizeof(bnd.SsdDesc) == 192
+    assert ctypes.sizeof(bnd.SsdDesc) == 208
     d = bnd.SsdDesc()
     ctypes.memset(ctypes.byref(d), 0x5A, ctypes.sizeof(d))
     lib.ssd_desc_init(ctypes.byref(d), 3, 5, 7, 64, 128, 7)
@@ -58,6 +58,7 @@ def test_desc_layout_matches_c(lib):
     assert d.dt_min == 0.0 and math.isinf(d.dt_max)
     assert d.z is None and d.dt_bias is None and d.initial_state is None and d.workspace is None
     assert d.workspace_bytes == 0 and d.chunks_per_wg == 0 and d.bc_dtype == bnd.SSD_F32
+    assert d.norm_weight is None and d.norm_eps == 0.0 and d.norm_groups == 0
     assert d.ev_main_begin is None and d.ev_main_end is None and d.cu_seqlens is None
     assert d.packed_tokens == 0 and d.error_flag is None
 
@@ -354,3 +355,56 @@ def test_noalloc_limit_matches_the_header():
     src = open(os.path.join(ROOT, "include", "ssd_mi355x.h")).read()
     m = re.search(r"#define SSD_FWD_NOALLOC_MAX_SCRATCH \(\(size_t\)(\d+) << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == bnd.NOALLOC_MAX_SCRATCH
+
+
+# ---------------------------------------------------------------- fused norm
+
+def _norm_desc(**kw):
+    d = _desc(**{k: v for k, v in kw.items() if k not in ("norm_eps", "norm_groups")})
+    d.norm_weight = FAKE
+    d.norm_eps = kw.get("norm_eps", 1e-5)
+    d.norm_groups = kw.get("norm_groups", 2)
+    return d
+
+
+@pytest.mark.parametrize("kw", [dict(norm_groups=0), dict(norm_groups=3), dict(norm_eps=0.0),
+                                dict(norm_eps=-1.0), dict(norm_eps=float("nan")),
+                                dict(norm_eps=float("inf"))])
+def test_invalid_norm_fields(lib, kw):
+    assert _call(lib, _norm_desc(**kw)) == bnd.SSD_ERR_INVALID_ARG
+
+
+def test_norm_groups_of_too_many_heads_are_unsupported(lib):
+    # k = H / norm_groups heads exchange partial sums: at most 32 (16 for
+    # 256-token chunks), so that a group's workgroups are resident together
+    assert _call(lib, _norm_desc(H=64, G=1, norm_groups=1)) == bnd.SSD_ERR_UNSUPPORTED
+    ok = _norm_desc(H=32, G=1, norm_groups=1)
+    assert _call(lib, ok, chunk=128) == bnd.SSD_ERR_WORKSPACE   # valid; no workspace given
+    assert _call(lib, _norm_desc(H=32, G=1, norm_groups=1), chunk=256) == bnd.SSD_ERR_UNSUPPORTED
+    assert _call(lib, _norm_desc(H=16, G=1, norm_groups=1), chunk=256) == bnd.SSD_ERR_WORKSPACE
+
+
+def test_misaligned_norm_weight(lib):
+    d = _norm_desc()
+    d.norm_weight = FAKE + 2
+    assert _call(lib, d) == bnd.SSD_ERR_INVALID_ARG
+
+
+def test_norm_workspace_holds_the_exchange(lib):
+    # B=1, L=128 (two 64-token chunks), H=4, G=2, norm_groups=2 (k=2): the
+    # epoch and count (one 256-byte unit), then a 64-bit record per head and
+    # token of every chunk, 1*2*4*64*8 bytes
+    plain = bnd.workspace_size(_desc(), 64)
+    fused = bnd.workspace_size(_norm_desc(), 64)
+    assert fused - plain == 256 + 4096
+    # one head per norm group: nothing to exchange, nothing extra
+    assert bnd.workspace_size(_norm_desc(norm_groups=4), 64) == plain
+
+
+def test_noalloc_refuses_more_records_than_its_norm_region(lib):
+    # H=4, chunk 64, L=128: 4096 record bytes per row; the region holds 256
+    # bytes plus that many rows' records, and one row more is refused
+    rows = (bnd.NOALLOC_SYNC_BYTES - 256) // 4096
+    st = lib.ssd_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 1, 0, FAKE, None, None,
+                             ctypes.byref(_norm_desc(B=rows + 1, L=128)))
+    assert st == bnd.SSD_ERR_WORKSPACE
