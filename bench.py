@@ -492,7 +492,7 @@ def fused_main(args, w: Workload) -> int:
                    "z": w.has_z, "io_dtype": w.io_dtype, "input_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name, "ssd_fwd_norm"),
+                     "traffic": measured_traffic(w.name + "+norm", "ssd_fwd"),
                      "kernel": "ssd_fwd with norm_weight (every kernel of one call)",
                      "kernel_ms": fused_ms, "algorithmic_bytes": abytes},
         "separate_chain": {"kernels": "ssd_fwd without the gate, then gated_rmsnorm_kernel",
@@ -555,20 +555,25 @@ def conv_main(args) -> int:
     print(f"[bench] causal conv1d {name}: B={B} D={D} S={S} W={W} sets={n_sets}",
           file=sys.stderr, flush=True)
     seed0 = (WORKLOADS[name].seed if name in WORKLOADS else 20269) * 1000 + 700
+    tok = args.conv_layout == "tokmajor"
     sets = []
     for k in range(n_sets):
         d = conv_inputs(B, D, S, W, seed0 + k, device=dev, has_state=True)
+        if tok:   # the same values, token-major [B, S, D]
+            d["x"] = d["x"].transpose(1, 2).contiguous()
         d["out"] = torch.empty_like(d["x"])
         d["fin"] = torch.empty_like(d["conv_state"])
         sets.append(d)
     stream = torch.cuda.current_stream().cuda_stream
     ev = HipEvents()
     copy_calibration(args.copy_calibration_mb, dev)
+    conv = ssd.causal_conv1d_tokmajor if tok else ssd.causal_conv1d
+    kernel = "causal_conv1d_tok_kernel" if tok else "causal_conv1d_vec_kernel"
 
     def step(k):
         d = sets[k % n_sets]
-        ssd.causal_conv1d(d["x"], d["w"], d["bias"], d["conv_state"], out=d["out"],
-                          return_final_state=True, final_state=d["fin"])
+        conv(d["x"], d["w"], d["bias"], d["conv_state"], out=d["out"], return_final_state=True,
+             final_state=d["fin"])
 
     for k in range(args.warmup):
         step(k)
@@ -602,14 +607,14 @@ def conv_main(args) -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"causal conv1d {name} [B={B}, D={D}, S={S}]", "B": B, "D": D,
+        "config": {"workload": f"causal conv1d {name} [B={B}, D={D}, S={S}]"
+                               + (" token-major [B, S, D]" if tok else ""), "B": B, "D": D,
                    "S": S, "W": W, "bias": True, "conv_state": True, "activation": "silu",
-                   "input_sets": n_sets},
+                   "layout": args.conv_layout, "input_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(name, "causal_conv1d_vec_kernel",
-                                                 "traffic_conv1d.json"),
-                     "kernel": "causal_conv1d_vec_kernel", "kernel_ms": kmean,
+                     "traffic": measured_traffic(name, kernel, "traffic_conv1d.json"),
+                     "kernel": kernel, "kernel_ms": kmean,
                      "algorithmic_bytes": abytes},
     }
     if not args.no_cpu_baseline:
@@ -732,6 +737,8 @@ def main(argv=None):
                                                         "causal_conv1d", "ssd_fwd_norm"],
                     help="ssd_fwd_norm: the forward with the gated RMSNorm fused into its "
                          "epilogue, timed against the forward and the norm kernel in sequence")
+    ap.add_argument("--conv-layout", default="channel", choices=["channel", "tokmajor"],
+                    help="--op causal_conv1d: [B, D, S] (channel) or token-major [B, S, D]")
     ap.add_argument("--mma", default="auto", choices=["auto", "f16", "bf16", "f32"],
                     help="MFMA operand precision; auto = bf16 for bf16 storage, else f16")
     ap.add_argument("--chunks-per-wg", type=int, default=0)
