@@ -268,6 +268,8 @@ def calibrate(dev: str) -> dict:
     lib.ssd_calib_mfma_f16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.ssd_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                    ctypes.c_void_p]
+    lib.ssd_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, device=dev)
@@ -295,12 +297,24 @@ def calibrate(dev: str) -> dict:
                                                     blocks_read, ctypes.c_void_p(stream))), 5)
     t_mfma = timed(lambda: check(lib.ssd_calib_mfma_f16(out.data_ptr(), blocks_mfma, iters,
                                                         ctypes.c_void_p(stream))), 3)
+    # the other matrix shapes: (kind, flops per wave per iteration)
+    shapes = {"mfma_f16_32x32x16_tflops": (1, 4 * 2 * 32 * 32 * 16),
+              "mfma_bf16_16x16x32_tflops": (2, 8 * 2 * 16 * 16 * 32),
+              "mfma_f32_16x16x4_tflops": (3, 8 * 2 * 16 * 16 * 4)}
+    per_shape = {}
+    for key, (kind, fpw) in shapes.items():
+        n_it = iters if kind != 3 else iters // 4
+        t = timed(lambda: check(lib.ssd_calib_mfma(out.data_ptr(), blocks_mfma, n_it, kind,
+                                                   ctypes.c_void_p(stream))), 3)
+        per_shape[key] = blocks_mfma * 4 * n_it * fpw / t / 1e12
     del src, dst, out
     flops = blocks_mfma * 4 * iters * 8 * 2 * 16 * 16 * 32
     return {"hbm_copy_gbs": 2 * nbytes / t_copy / 1e9, "hbm_read_gbs": nbytes / t_read / 1e9,
-            "mfma_f16_tflops": flops / t_mfma / 1e12,
+            "mfma_f16_tflops": flops / t_mfma / 1e12, **per_shape,
             "how": "1 GiB device copy (read + write bytes), 1 GiB streaming read, "
-                   f"{blocks_mfma} x 256-thread blocks of back-to-back 16x16x32 fp16 MFMAs"}
+                   f"{blocks_mfma} x 256-thread blocks of back-to-back MFMAs on registers "
+                   "(16x16x32 fp16 with 8 accumulators per wave; also 32x32x16 fp16 with 4, "
+                   "16x16x32 bf16 and 16x16x4 fp32 with 8)"}
 
 
 def copy_calibration(mb: int, dev: str) -> None:
@@ -640,6 +654,7 @@ def bwd_main(args) -> int:
         return 2
     dev = "cuda:0"
     print(f"[bench] SSD backward {w.name} {w.shape_str()}", file=sys.stderr, flush=True)
+    copy_calibration(args.copy_calibration_mb, dev)
     d = {k: (None if v is None else v.to(dev)) for k, v in make_inputs(w).items()}
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed * 1000 + 900)
@@ -692,6 +707,18 @@ def bwd_main(args) -> int:
                      "kernel": "ssd_bwd_chunk_kernel", "kernel_ms": kmean,
                      "algorithmic_flops": flops},
     }
+    if not args.no_calibration:
+        print("[bench] calibrating the GPU's delivered peaks", file=sys.stderr, flush=True)
+        try:
+            cal = calibrate(dev)
+        except (OSError, RuntimeError) as e:
+            cal = {"error": str(e)}
+        if "mfma_f32_16x16x4_tflops" in cal:
+            rec["roofline"]["calibrated"] = {
+                "peak": cal["mfma_f32_16x16x4_tflops"], "unit": "TFLOP/s",
+                "frac": achieved / cal["mfma_f32_16x16x4_tflops"],
+                "of": "this GPU's measured back-to-back 16x16x4 fp32 MFMA rate"}
+        rec["calibration"] = cal
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = bwd_cpu_baseline(w, args.cpu_baseline_seconds)

@@ -304,11 +304,24 @@ __device__ __forceinline__ void stage_tile2(const Tile2 &o, float *dst) {
   }
 }
 
+// Workgroup id -> (b, h) pair.  Workgroup n runs on XCD n % 8; the pairs are
+// dealt to the XCDs in contiguous runs (the grid is 8 * ceil(B*H / 8)), so
+// the heads that share one B/C group run side by side on one XCD and read
+// their B and C rows through its L2 instead of each from HBM.  Returns -1
+// for the padding workgroups past B*H.
+__device__ __forceinline__ int64_t bwd_pair(int64_t total) {
+  const int64_t n = blockIdx.x, per = (total + 7) / 8;
+  const int64_t t = (n % 8) * per + n / 8;
+  return t < total ? t : -1;
+}
+
 // Forward pass that stores the state entering every chunk.
 __global__ __launch_bounds__(256) void ssd_bwd_states_kernel(BwdParams p) {
   __shared__ float sX[kQ * kLd], sB[kQ * kLd];
   __shared__ ChunkScalars cs;
-  const int64_t bh = blockIdx.x, b = bh / p.H, h = bh % p.H;
+  const int64_t bh = bwd_pair(p.batch * p.H);
+  if (bh < 0) return;
+  const int64_t b = bh / p.H, h = bh % p.H;
   const int64_t g = h / (p.H / p.G);
   const uint32_t H = (uint32_t)p.H, G = (uint32_t)p.G, L = (uint32_t)p.L;
   const rsrc_t rx = make_rsrc(p.x + b * p.L * p.H * kP, L * H * kP * 4u);
@@ -373,7 +386,9 @@ __global__ __launch_bounds__(kT8) void ssd_bwd_chunk_kernel(BwdParams p) {
   __shared__ float sVec[6][kQ];  // q, r, w, v, dLam, (spare)
   __shared__ ChunkScalars cs;
 
-  const int64_t bh = blockIdx.x, b = bh / p.H, h = bh % p.H;
+  const int64_t bh = bwd_pair(p.batch * p.H);
+  if (bh < 0) return;
+  const int64_t b = bh / p.H, h = bh % p.H;
   const int64_t g = h / (p.H / p.G);
   const uint32_t H = (uint32_t)p.H, G = (uint32_t)p.G, L = (uint32_t)p.L;
   const rsrc_t rx = make_rsrc(p.x + b * p.L * p.H * kP, L * H * kP * 4u);
@@ -804,7 +819,7 @@ ssd_status ssd_bwd(const float *x, const float *dt, const float *A, const float 
   p.dt_softplus = dt_softplus ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const unsigned nbh = (unsigned)(d->batch * d->nheads);
+  const unsigned nbh = (unsigned)((d->batch * d->nheads + 7) / 8 * 8);  // see bwd_pair
   hipLaunchKernelGGL(ssd_bwd_states_kernel, dim3(nbh), dim3(256), 0, st, p);
   // the descriptor's measurement events bracket the main (chunk) kernel
   if (d->ev_main_begin && hipEventRecord(static_cast<hipEvent_t>(d->ev_main_begin), st) != hipSuccess)
