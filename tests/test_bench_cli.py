@@ -32,3 +32,14 @@ def test_quantile_and_algorithmic_counts():
     nc = 2048 // 128
     assert bench.algorithmic_flops(w) == 2 * 4 * nc * (G * 128 * 128 * N + H * 128 * 128 * P
                                                        + 2 * H * 128 * N * P)
+
+
+def test_processes_run_children_and_stop_on_a_failed_one():
+    # without a GPU the first child exits 2 ("needs a GPU"); the parent stops
+    # there with that code and prints no JSON line
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--processes", "3",
+                        "--steps", "1"], capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert r.returncode == 2
+    assert "process 1 of 3" in r.stderr and "process 1 failed" in r.stderr
+    assert "process 2 of 3" not in r.stderr
+    assert r.stdout.strip() == ""
