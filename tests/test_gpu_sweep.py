@@ -11,6 +11,12 @@ final_state with the fp64 oracle's token recurrence on the same stored
 values.  The bar is the parity bar of test_gpu_parity.py (2e-3, 1.6e-2 and
 1e-4 of max|oracle| for fp16, bf16 and fp32 operands), plus bf16's storage
 rounding (2^-8) when out is bf16.
+
+A second sweep draws configurations of the forward with the gated RMSNorm
+fused into its epilogue (1 to 32 heads per norm group, every chunk size,
+chunk groups split over workgroups, fp32 or bf16 storage, every operand
+precision) and holds them to the propagated bound of test_gpu_norm_fused.py
+against the oracle chain (the token recurrence, then the gated norm).
 """
 import math
 import sys
@@ -97,3 +103,43 @@ def test_random_configuration_matches_the_oracle(gpu_lib, case):
     check(out.float().cpu().numpy(), ref_out, tol + (2 ** -8 if c["out_bf16"] else 0.0), "out")
     if c["ret_final"]:
         check(fin.cpu().numpy(), ref_fin, tol, "final_state")
+
+
+# ------------------------------------------------------------------ fused gated RMSNorm
+
+NNORM = 40
+
+
+def draw_norm(case: int):
+    """A configuration of the forward with the norm fused into its epilogue:
+    k heads per norm group (at most 32, at most 16 with 256-token chunks)."""
+    r = np.random.RandomState(72000 + case)
+    pick = lambda xs: xs[r.randint(len(xs))]
+    chunk = int(pick([64, 128, 256]))
+    kmax = 16 if chunk == 256 else 32
+    H = int(pick([2, 4, 6, 8, 12, 16, 32]))
+    ks = [k for k in (1, 2, 3, 4, 6, 8, 16, 32) if H % k == 0 and k <= kmax]
+    k = int(pick(ks))
+    return dict(B=int(r.randint(1, 3)), L=int(r.randint(1, 600)), H=H, k=k,
+                G=int(pick([g for g in (1, 2, 4) if H % g == 0])), N=int(pick([64, 128])),
+                chunk=chunk, cpw=int(pick([0, 0, 1, 2])),
+                io=str(pick(["f32", "f32", "bf16"])), mma=str(pick(["f16", "f16", "bf16", "f32"])),
+                D=bool(r.rand() < 0.5), z=bool(r.rand() < 0.6), h0=bool(r.rand() < 0.4),
+                dt_bias=bool(r.rand() < 0.5))
+
+
+@pytest.mark.parametrize("case", range(NNORM))
+def test_random_fused_norm_configuration_matches_the_oracle_chain(gpu_lib, case):
+    from test_gpu_norm_fused import Chain, fused, norm_weight
+    c = draw_norm(case)
+    _say(f"[case] fused-norm sweep {case}: {c}")
+    d = random_inputs(c["B"], c["L"], c["H"], 64, c["N"], c["G"], seed=73000 + case,
+                      has_D=c["D"], has_z=c["z"], has_h0=c["h0"], io_dtype=c["io"],
+                      dt_bias=c["dt_bias"])
+    w = norm_weight(c["H"] * 64, 74000 + case)
+    ngroups = c["H"] // c["k"]
+    ref = Chain(d, w, ngroups)
+    out, fin = fused(gpu_lib, d, w, ngroups, c["chunk"], mma=c["mma"], chunks_per_wg=c["cpw"])
+    tol = TOL[c["mma"]]
+    ref.check(out.cpu().numpy(), tol)
+    check(fin.cpu().numpy(), ref.fin, tol, "final_state")
