@@ -17,6 +17,10 @@ fused into its epilogue (1 to 32 heads per norm group, every chunk size,
 chunk groups split over workgroups, fp32 or bf16 storage, every operand
 precision) and holds them to the propagated bound of test_gpu_norm_fused.py
 against the oracle chain (the token recurrence, then the gated norm).
+Two more draw packed variable-length sequences (empty, one-token and
+chunk-edge lengths among them) against the per-sequence oracle, and the
+backward's scope (P = N = chunk = 64, fp32) against the fp64 autograd
+oracle at the backward's 1e-4 bound.
 """
 import math
 import sys
@@ -143,3 +147,87 @@ def test_random_fused_norm_configuration_matches_the_oracle_chain(gpu_lib, case)
     tol = TOL[c["mma"]]
     ref.check(out.cpu().numpy(), tol)
     check(fin.cpu().numpy(), ref.fin, tol, "final_state")
+
+
+# ------------------------------------------------------------------ packed sequences
+
+NPACK = 30
+
+
+def draw_packed(case: int):
+    """Packed variable-length sequences: 1 to 12 sequences of 0 to 700 tokens
+    (empty and one-token ones included), every chunk size, chunk groups per
+    workgroup from the plan or forced small (several groups per sequence)."""
+    r = np.random.RandomState(75000 + case)
+    pick = lambda xs: xs[r.randint(len(xs))]
+    n = int(r.randint(1, 13))
+    lens = tuple(int(pick([0, 1, 2, 63, 64, 65])) if r.rand() < 0.3 else int(r.randint(1, 700))
+                 for _ in range(n))
+    if sum(lens) == 0:
+        lens = lens[:-1] + (5,)
+    H = int(pick([2, 4, 6, 8]))
+    return dict(lens=lens, H=H, G=int(pick([g for g in (1, 2, 3, 4) if H % g == 0])),
+                N=int(pick([64, 128])), chunk=int(pick([64, 128, 256])),
+                cpw=int(pick([0, 0, 1, 2])), mma=str(pick(["f16", "f16", "f32"])))
+
+
+@pytest.mark.parametrize("case", range(NPACK))
+def test_random_packed_sequences_match_the_oracle(gpu_lib, case):
+    from oracle import ssd_varlen
+    from workloads import packed_inputs
+    c = draw_packed(case)
+    _say(f"[case] packed sweep {case}: {c}")
+    d = packed_inputs(c["lens"], c["H"], 64, c["N"], c["G"], seed=76000 + case, has_D=True,
+                      has_z=True, has_h0=True, dt_bias=True)
+    g = {k: (None if v is None else v.cuda()) for k, v in d.items()}
+    out, fin = gpu_lib.ssd_fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], c["chunk"], D=g["D"],
+                               z=g["z"], dt_bias=g["dt_bias"], initial_states=g["initial_states"],
+                               dt_softplus=True, return_final_state=True, mma=c["mma"],
+                               chunks_per_wg=c["cpw"], cu_seqlens=g["cu_seqlens"])
+    torch.cuda.synchronize()
+    ref_o, ref_f = ssd_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["cu_seqlens"], D=d["D"],
+                              z=d["z"], dt_bias=d["dt_bias"], initial_states=d["initial_states"],
+                              dt_softplus=True)
+    tol = TOL[c["mma"]]
+    check(out[0].float().cpu().numpy(), ref_o, tol, "out")
+    check(fin.cpu().numpy(), ref_f, tol, "final_state")
+
+
+# ------------------------------------------------------------------ backward
+
+NBWD = 12
+
+
+def draw_bwd(case: int):
+    """The backward's scope (P = N = chunk = 64, fp32): random batch, length,
+    heads and groups, optional D, z, dt_bias, initial state and final-state
+    gradient, softplus or a dt limit."""
+    r = np.random.RandomState(77000 + case)
+    pick = lambda xs: xs[r.randint(len(xs))]
+    H = int(pick([1, 2, 4, 6]))
+    return dict(B=int(r.randint(1, 3)), L=int(r.randint(1, 330)), H=H,
+                G=int(pick([g for g in (1, 2, 3) if H % g == 0])),
+                D=bool(r.rand() < 0.5), z=bool(r.rand() < 0.5), h0=bool(r.rand() < 0.5),
+                dt_bias=bool(r.rand() < 0.5), dfin=bool(r.rand() < 0.6),
+                softplus=bool(r.rand() < 0.7), limit=bool(r.rand() < 0.3))
+
+
+@pytest.mark.parametrize("case", range(NBWD))
+def test_random_backward_configuration_matches_the_oracle(gpu_lib, case):
+    from test_gpu_bwd import NAMES, grads_both, rel_err
+    c = draw_bwd(case)
+    _say(f"[case] backward sweep {case}: {c}")
+    d = random_inputs(c["B"], c["L"], c["H"], 64, 64, c["G"], seed=78000 + case, has_D=c["D"],
+                      has_z=c["z"], has_h0=c["h0"], dt_bias=c["dt_bias"])
+    gen = torch.Generator().manual_seed(79000 + case)
+    dout = torch.randn(c["B"], c["L"], c["H"], 64, generator=gen)
+    dfin = torch.randn(c["B"], c["H"], 64, 64, generator=gen) if c["dfin"] else None
+    limit = (0.5, 1.2) if c["limit"] else (0.0, math.inf)
+    got, ref = grads_both(gpu_lib, d, dout, dfin, softplus=c["softplus"], limit=limit)
+    for k in NAMES:
+        if ref.get(k) is None:
+            assert got.get(k) is None, k
+            continue
+        e = rel_err(got[k].cpu().numpy(), ref[k])
+        _say(f"    {k}: max_err/max_ref={e:.3e}")
+        assert e <= 1e-4, f"{k}: {e:.3e} > 1e-4"
