@@ -97,6 +97,22 @@ __device__ __forceinline__ f32x4 mma(const f32x8 &a, const f32x8 &b, f32x4 c) {
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// softplus(u) = max(u, 0) + log1p(e) with e = exp(-|u|) in (0, 1], without
+// the library log1p (about 70 instructions).  Below 1/16, log1p(e) is its
+// alternating series to e^5 (truncation below e^6/6, under 1.7e-7 of the
+// result); from 1/16 on, the hardware log2 of v = 1 + e times ln 2, with the
+// rounding of v undone by the factor e / (v - 1) (v - 1 is exact), so the
+// result keeps a few ulp where the plain log of 1 + e would lose the digits
+// of a small e.
+__device__ __forceinline__ float softplus_f(float u) {
+  const float e = __expf(-fabsf(u));
+  const float v = 1.f + e;
+  const float big = __builtin_amdgcn_logf(v) * 0.6931471805599453f *
+                    (e * __builtin_amdgcn_rcpf(v - 1.f));
+  const float small = e * (1.f - e * (0.5f - e * (1.f / 3.f - e * (0.25f - e * 0.2f))));
+  return fmaxf(u, 0.f) + (e < 0.0625f ? small : big);
+}
+
 // ---------------------------------------------------------------- buffer access
 // Every tensor of one batch row is addressed through a raw buffer resource
 // (base in SGPRs, 32-bit byte offsets per lane).  The hardware range check
@@ -432,8 +448,9 @@ __device__ __forceinline__ void chunk_prep(const Params &p, uint32_t t0, uint64_
     float u = cl.dts[lane + 64 * m] + bias;
     // softplus as max(u, 0) + log1p(exp(-|u|)): no cancellation for negative
     // u (where log(1 + exp(u)) loses the digits of a small step) and no
-    // overflow for large u; the backward uses the same form
-    if (p.dt_softplus) u = fmaxf(u, 0.f) + log1pf(__expf(-fabsf(u)));
+    // overflow for large u; the backward uses the same form (with the
+    // library log1p)
+    if (p.dt_softplus) u = softplus_f(u);
     const float delta = (t0 + lane + 64 * m < len) ? fminf(fmaxf(u, p.dt_min), p.dt_max) : 0.f;
     const float a = delta * a_h * kLog2e;
     big |= fabsf(a) > 7.f;
