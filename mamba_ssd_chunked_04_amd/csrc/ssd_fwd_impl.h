@@ -97,6 +97,22 @@ __device__ __forceinline__ f32x4 mma(const f32x8 &a, const f32x8 &b, f32x4 c) {
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// Two floats rounded to the operand type E as one packed conversion
+// (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 on gfx950, round to nearest even;
+// for E = float a copy).
+template <class E> struct Pair2 { E x, y; };
+template <class E>
+__device__ __forceinline__ Pair2<E> cvt2(float a, float b) {
+  if constexpr (sizeof(E) == 4) {
+    return {a, b};
+  } else {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef E e2 __attribute__((ext_vector_type(2)));
+    const e2 v = __builtin_convertvector((f2){a, b}, e2);
+    return {v.x, v.y};
+  }
+}
+
 // softplus(u) = max(u, 0) + log1p(e) with e = exp(-|u|) in (0, 1], without
 // the library log1p (about 70 instructions).  Below 1/16, log1p(e) is its
 // alternating series to e^5 (truncation below e^6/6, under 1.7e-7 of the
@@ -1493,7 +1509,26 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
             }
           }
           frag mf;
-          if (jbase + 31 > row0) {  // the sub-block meets the diagonal: mask j > i
+          // bf16 operands: masked in fp32, then rounded two at a time
+          // (v_cvt_pk_bf16_f32; 1% on the gated workload); the fp16 form
+          // below measured faster as the compiler schedules it
+          if constexpr (MM == kMmaBF16) {
+            if (jbase + 31 > row0) {  // the sub-block meets the diagonal: mask j > i
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                ma[r] = ja0 + r <= i ? ma[r] : 0.f;
+                mc[r] = ja0 + 16 + r <= i ? mc[r] : 0.f;
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const Pair2<E> pa = cvt2<E>(ma[r], ma[r + 1]), pc = cvt2<E>(mc[r], mc[r + 1]);
+              mf[r] = pa.x;
+              mf[r + 1] = pa.y;
+              mf[4 + r] = pc.x;
+              mf[4 + r + 1] = pc.y;
+            }
+          } else if (jbase + 31 > row0) {  // the sub-block meets the diagonal: mask j > i
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               mf[r] = (E)(ja0 + r <= i ? ma[r] : 0.f);
