@@ -141,6 +141,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
                                            0x00020000);
 }
 
+// Cache-policy bit of buffer operations for device scope: such a store is
+// written through its XCD's L2 (visible to every XCD once complete, and
+// left clean, so a kernel's end has less to write back), such a load reads
+// past it.
+constexpr int kSc1 = 16;
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) {
   return __uint_as_float(v << 16);
 }
@@ -267,7 +273,11 @@ struct Params {
 // u on XCD u % 8), so long and short sequences spread over all of them; the
 // grid then has 8 * hpg * ceil(units / 8) workgroups (tile_grid).  With
 // `late_first` the chunk groups are dealt from the last one down (later
-// groups have more to do before their first chunk).
+// groups have more to do before their first chunk): when the main pass
+// folds an even number of groups itself, a dense call's late group ng-1-i is
+// dealt with its early partner i on one XCD, late members first, so each XCD
+// holds the same mix of long and short prologues and a CU's two workgroups
+// tend to be such a pair (headline main pass 39.4 -> 38.3 us).
 __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_here, int64_t &b,
                                             int64_t &h, int64_t &j, bool late_first = false) {
   const int64_t total = p.batch * p.H * ngroups_here;
@@ -277,6 +287,23 @@ __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_her
   if (p.cu_seqlens) {
     const int64_t k = n / 8;
     T = ((k / hpg) * 8 + n % 8) * hpg + k % hpg;
+  } else if (late_first && ngroups_here % 2 == 0 && !p.chained) {
+    // tiles paired, late group ng-1-i with early group i (same b, g and
+    // head), in the order (b, i, g, head in group); each XCD takes a
+    // contiguous run of pairs and dispatches its late members first, then
+    // the early ones in the same order (tile_grid workgroups)
+    const int64_t pairs = total / 2, pp = (pairs + 7) / 8;
+    const int64_t k = n / 8, half = k / pp, pr = (n % 8) * pp + k % pp;
+    if (half > 1 || pr >= pairs) return false;
+    const int64_t hh = pr % hpg;
+    int64_t rest = pr / hpg;
+    const int64_t g = rest % p.G;
+    rest /= p.G;
+    const int64_t i = rest % (ngroups_here / 2);
+    b = rest / (ngroups_here / 2);
+    j = half == 0 ? ngroups_here - 1 - i : i;
+    h = g * hpg + hh;
+    return true;
   } else {
     const int64_t per = (total + 7) / 8;
     T = (n % 8) * per + n / 8;
@@ -981,11 +1008,17 @@ __global__ __launch_bounds__(256 * HW) void ssd_group_state_kernel(Params p) {
   const int64_t slot = bh * (p.ngroups - 1) + j;
   float *dst = p.grp_state + slot * (int64_t)(kP * N);
   // (the four rows of a fragment are consecutive in the record, and
-  // consecutive lanes' fragments adjacent: one coalesced 16-byte store each)
+  // consecutive lanes' fragments adjacent: one coalesced 16-byte store each;
+  // device scope, so the aggregates are in memory when the last workgroup
+  // ends instead of dirty in the L2s: 20.6 -> 19.4 us before the headline's
+  // main pass)
   constexpr int WM = main_waves<Q>();
+  const rsrc_t rd = make_rsrc(dst, (uint32_t)(kP * N * 4));
 #pragma unroll
   for (int t = 0; t < NN; ++t)
-    *reinterpret_cast<f32x4 *>(dst + rec_index<N, WM>(16 * wl + 4 * lq, 16 * t + lr)) = sacc[t];
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, sacc[t]), rd,
+                                           rec_index<N, WM>(16 * wl + 4 * lq, 16 * t + lr) * 4, 0,
+                                           kSc1);
   if (tid == 0) p.grp_lam[slot] = lgrp;
 }
 
@@ -1007,10 +1040,26 @@ __global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p) {
   }
   const int64_t ng1 = p.ngroups - 1;
   const int64_t ng1_row = row_groups(p, row_span(p, bh / p.H).len) - 1;  // filled slots
-  for (int64_t jj = 0; jj < ng1_row; ++jj) {
-    const int64_t slot = bh * ng1 + jj;
-    S = fast_exp2(p.grp_lam[slot]) * S + p.grp_state[slot * PN + e];
-    p.grp_state[slot * PN + e] = S;
+  // KS slots at a time: their loads are all in flight before the chain uses
+  // them (a slot index past the filled ones repeats the last, unused); the
+  // entering states are stored with device scope, like the aggregates
+  constexpr int KS = 8;
+  auto slot_rsrc = [&](int64_t jj) { return make_rsrc(p.grp_state + (bh * ng1 + jj) * PN, PN * 4); };
+  for (int64_t j0 = 0; j0 < ng1_row; j0 += KS) {
+    float v[KS], lam[KS];
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      const int64_t jj = j0 + q < ng1_row ? j0 + q : ng1_row - 1;
+      v[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(slot_rsrc(jj), (uint32_t)e * 4, 0, 0));
+      lam[q] = p.grp_lam[bh * ng1 + jj];
+    }
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      if (j0 + q >= ng1_row) break;
+      S = fast_exp2(lam[q]) * S + v[q];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S), slot_rsrc(j0 + q), (uint32_t)e * 4, 0,
+                                            kSc1);
+    }
   }
 }
 
@@ -1035,7 +1084,6 @@ __global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p) {
 // far below the workgroups an XCD holds).  The wait is still bounded (20 ms
 // of the 100 MHz real-time counter): on a time-out *error_flag is set to 2
 // and those rows come out undefined, but the kernel ends.
-constexpr int kSc1 = 16;                    // cache-policy bit of buffer ops: device scope
 constexpr uint64_t kNormTicks = 2000000;    // 20 ms
 
 // Sum over the 16 lanes of a quarter-wave (lanes 16q .. 16q+15); every lane
@@ -1658,19 +1706,21 @@ struct Plan {
 
 // Workgroups covering `ngroups_here` chunk groups of every (b, h), as
 // decode_tile deals them.
-inline int64_t tile_grid(const Params &p, int64_t ngroups_here) {
+inline int64_t tile_grid(const Params &p, int64_t ngroups_here, bool late_first = false) {
   const int64_t hpg = p.H / p.G;
   if (p.cu_seqlens) {
     const int64_t units = p.batch * p.G * ngroups_here;
     return 8 * hpg * ((units + 7) / 8);
   }
-  return 8 * ((p.batch * p.H * ngroups_here + 7) / 8);
+  const int64_t total = p.batch * p.H * ngroups_here;
+  if (late_first && ngroups_here % 2 == 0 && !p.chained) return 16 * ((total / 2 + 7) / 8);
+  return 8 * ((total + 7) / 8);
 }
 
 template <int Q, int N, int MM, class IO>
 ssd_status launch_all(const Params &prm, const Plan &pl, hipStream_t stream, const ssd_desc *d) {
   const int64_t bh = prm.batch * prm.H;
-  const int64_t g2 = tile_grid(prm, pl.ngroups);  // the largest grid, checked before any launch
+  const int64_t g2 = tile_grid(prm, pl.ngroups, true);  // the largest grid, checked before any launch
   if (g2 > (int64_t)UINT32_MAX) return SSD_ERR_UNSUPPORTED;
   if (pl.ngroups > 1) {
     // two heads of a B/C group per workgroup when the group has an even
