@@ -265,6 +265,16 @@ struct Params {
   int norm_k;
 };
 
+// Quotient and remainder of non-negative values below 2^32 (tile indices,
+// head, group and chunk counts): the 32-bit sequence is a fraction of the
+// 64-bit one, and these sit before a workgroup's first loads.
+__device__ __forceinline__ int64_t udiv32(int64_t a, int64_t b) {
+  return (int64_t)((uint32_t)a / (uint32_t)b);
+}
+__device__ __forceinline__ int64_t umod32(int64_t a, int64_t b) {
+  return (int64_t)((uint32_t)a % (uint32_t)b);
+}
+
 // Workgroup id -> (b, h, chunk group).  Tiles are ordered (b, group, g, head
 // in group); workgroup n runs on XCD n % 8.  Dense calls deal the tiles in
 // contiguous runs to the XCDs, so the heads that share one B/C group run side
@@ -277,7 +287,9 @@ struct Params {
 // folds an even number of groups itself, a dense call's late group ng-1-i is
 // dealt with its early partner i on one XCD, late members first, so each XCD
 // holds the same mix of long and short prologues and a CU's two workgroups
-// tend to be such a pair (headline main pass 39.4 -> 38.3 us).
+// tend to be such a pair (headline main pass 39.4 -> 38.3 us).  (Its
+// divisions stay 64-bit: with udiv32 here the compiler spilled scalar
+// registers inside the block loop of the 256-token gated kernel, 1% slower.)
 __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_here, int64_t &b,
                                             int64_t &h, int64_t &j, bool late_first = false) {
   const int64_t total = p.batch * p.H * ngroups_here;
@@ -293,14 +305,14 @@ __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_her
     // contiguous run of pairs and dispatches its late members first, then
     // the early ones in the same order (tile_grid workgroups)
     const int64_t pairs = total / 2, pp = (pairs + 7) / 8;
-    const int64_t k = n / 8, half = k / pp, pr = (n % 8) * pp + k % pp;
+    const int64_t k = n / 8, half = udiv32(k, pp), pr = (n % 8) * pp + umod32(k, pp);
     if (half > 1 || pr >= pairs) return false;
-    const int64_t hh = pr % hpg;
-    int64_t rest = pr / hpg;
-    const int64_t g = rest % p.G;
-    rest /= p.G;
-    const int64_t i = rest % (ngroups_here / 2);
-    b = rest / (ngroups_here / 2);
+    const int64_t hh = umod32(pr, hpg);
+    int64_t rest = udiv32(pr, hpg);
+    const int64_t g = umod32(rest, p.G);
+    rest = udiv32(rest, p.G);
+    const int64_t i = umod32(rest, ngroups_here / 2);
+    b = udiv32(rest, ngroups_here / 2);
     j = half == 0 ? ngroups_here - 1 - i : i;
     h = g * hpg + hh;
     return true;
@@ -353,10 +365,10 @@ __device__ __forceinline__ bool offsets_break_contract(const Params &p, int64_t 
 // Chunks of a row and the chunk groups that hold them; an empty row keeps
 // one group, which writes its final state (the initial state).
 __device__ __forceinline__ int64_t row_chunks(const Params &p, int64_t len) {
-  return (len + p.Q - 1) / p.Q;
+  return udiv32(len + p.Q - 1, p.Q);
 }
 __device__ __forceinline__ int64_t row_groups(const Params &p, int64_t len) {
-  const int64_t ng = (row_chunks(p, len) + p.cpg - 1) / p.cpg;
+  const int64_t ng = udiv32(row_chunks(p, len) + p.cpg - 1, p.cpg);
   return ng < 1 ? 1 : ng;
 }
 
@@ -835,17 +847,17 @@ __device__ __forceinline__ int nblocks(int Qc) { return (Qc + kJB - 1) / kJB; }
 // share an L2; packed calls deal them round-robin (rows differ in length).
 __device__ __forceinline__ bool decode_state_tile(const Params &p, int hw, int64_t &b, int64_t &g,
                                                   int64_t &s, int64_t &j) {
-  const int64_t sets = (p.H / p.G) / hw, ng1 = p.ngroups - 1;
+  const int64_t sets = udiv32(p.H, p.G) / hw, ng1 = p.ngroups - 1;
   const int64_t total = p.batch * p.G * ng1 * sets;
   const int64_t n = blockIdx.x;
   const int64_t T = p.cu_seqlens ? n : (n % 8) * ((total + 7) / 8) + n / 8;
   if (T >= total) return false;
-  s = T % sets;
-  int64_t rest = T / sets;
-  j = rest % ng1;
-  rest /= ng1;
-  g = rest % p.G;
-  b = rest / p.G;
+  s = umod32(T, sets);
+  int64_t rest = udiv32(T, sets);
+  j = umod32(rest, ng1);
+  rest = udiv32(rest, ng1);
+  g = umod32(rest, p.G);
+  b = udiv32(rest, p.G);
   return true;
 }
 
@@ -873,7 +885,7 @@ __global__ __launch_bounds__(256 * HW) void ssd_group_state_kernel(Params p) {
   if (j >= row_groups(p, rs.len) - 1) return;  // the row's last group, or past its end
   const int hh = (int)(threadIdx.x >> 8);       // head of the set this thread works for
   const int tid = (int)(threadIdx.x & 255);     // thread index within that head's four waves
-  const int64_t hpg = p.H / p.G;
+  const int64_t hpg = udiv32(p.H, p.G);
   const int64_t h = g * hpg + s * HW + hh;
   const int64_t bh = b * p.H + h;
   const SeqView<N, IO> sv(p, rs, h, g);
@@ -1039,7 +1051,7 @@ __global__ __launch_bounds__(256) void ssd_group_passing_kernel(Params p) {
     S = p.h0[bh * PN + row * N + col];
   }
   const int64_t ng1 = p.ngroups - 1;
-  const int64_t ng1_row = row_groups(p, row_span(p, bh / p.H).len) - 1;  // filled slots
+  const int64_t ng1_row = row_groups(p, row_span(p, udiv32(bh, p.H)).len) - 1;  // filled slots
   // KS slots at a time: their loads are all in flight before the chain uses
   // them (a slot index past the filled ones repeats the last, unused); the
   // entering states are stored with device scope, like the aggregates
@@ -1199,7 +1211,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lq = lane >> 4;
   const int pt0 = RS::pt0(w);
-  const int64_t g = h / (p.H / p.G);
+  const int64_t g = udiv32(h, udiv32(p.H, p.G));
   const SeqView<N, IO> sv(p, rs, h, g);
   const uint64_t lhp = (uint64_t)rs.len * p.H * kP, ohp = (uint64_t)rs.start * p.H * kP;
   const int osz = p.out_bf16 ? 2 : 4, zsz = p.z_bf16 ? 2 : 4;
@@ -1339,7 +1351,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssd_chunk_scan_kernel(Params p) {
     return make_rsrc(nx ? p.norm_rec + ((b * p.nchk_row + cc) * p.H) * Q : nullptr,
                      nx ? (uint32_t)(p.H * Q * 8) : 0u);
   };
-  const int64_t h0n = h - h % p.norm_k;  // the norm group's first head
+  const int64_t h0n = h - umod32(h, p.norm_k);  // the norm group's first head
   // the sums over the group's members for rows crow .. crow+3 of chunk cc
   // (lane lr takes members lr, lr+16; then the quarter-wave adds them up)
   auto norm_sums = [&](int64_t cc, int crow) {
