@@ -207,14 +207,17 @@ __global__ __launch_bounds__(256) void causal_conv1d_step_kernel(ConvArgs a) {
 // are xs elements apart (channels 0..D-1 of each row are read, so x may be a
 // column range of a wider projection output), out [B, S, D] dense, the conv
 // state x_prev / final_state [B, D, W-1] as above.  A wave owns 256 channels
-// (4 consecutive ones per lane) and walks 32 consecutive steps: every load
+// (4 consecutive ones per lane) and walks TS consecutive steps: every load
 // and store of a step is one 1 KB row segment, the W-1 steps before the
 // current one stay in registers, and the W-1 steps before the wave's first
 // step come from x (or x_prev before t = 0).  Sixteen steps are loaded
 // ahead.  Consecutive workgroups take consecutive 256-channel blocks of the
 // same steps, so the chip reads and writes whole token rows in address order
 // (5-13% faster on the larger shapes than walking one channel block's steps
-// first; 16 steps ahead instead of 8 gave another 1-3%).
+// first; 16 steps ahead instead of 8 gave another 1-3%).  TS is 32, or 16
+// when 32-step waves would give the chip fewer than two workgroups per CU
+// (twice the waves for the same bytes: the page's test shape 23.7 -> 22.7
+// us; with 512 workgroups already, [4, 2048, 2048] got 9% slower).
 constexpr int kTokSteps = 32;   // steps per wave
 constexpr int kTokAhead = 16;   // steps loaded ahead
 
@@ -223,10 +226,10 @@ struct TokArgs {
   float *out, *fin;
   int64_t batch, dim, S, xs;
   int act;
-  uint32_t cblk, sblk;  // 256-channel blocks, 128-step blocks (four waves each)
+  uint32_t cblk, sblk;  // 256-channel blocks, 4*TS-step blocks (four waves each)
 };
 
-template <int W>
+template <int W, int TS>
 __global__ __launch_bounds__(256) void causal_conv1d_tok_kernel(TokArgs a) {
   const uint32_t n = blockIdx.x;
   const uint32_t cb = n % a.cblk, sb = (n / a.cblk) % a.sblk;
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(256) void causal_conv1d_tok_kernel(TokArgs a) {
   const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
   const int64_t c = 256 * (int64_t)cb + 4 * lane;         // this lane's first channel
   const bool live = c < a.dim;                             // D % 4 == 0: all four or none
-  const int64_t t0 = (int64_t)sb * 4 * kTokSteps + wave * kTokSteps;
+  const int64_t t0 = (int64_t)sb * 4 * TS + wave * TS;
   if (t0 >= a.S) return;
   const rsrc_t rx = make_rsrc(a.x + b * a.S * a.xs, (uint32_t)(a.S * a.xs * 4));
   const rsrc_t ro = make_rsrc(a.out + b * a.S * a.dim, (uint32_t)(a.S * a.dim * 4));
@@ -267,12 +270,12 @@ __global__ __launch_bounds__(256) void causal_conv1d_tok_kernel(TokArgs a) {
   for (int k = 0; k < kTokAhead; ++k)
     buf[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff(t0 + k), 0, kStream));
 #pragma unroll
-  for (int g = 0; g < kTokSteps / kTokAhead; ++g) {
+  for (int g = 0; g < TS / kTokAhead; ++g) {
 #pragma unroll
     for (int k = 0; k < kTokAhead; ++k) {
       const int64_t t = t0 + g * kTokAhead + k;
       win[W - 1] = buf[k];
-      if (g + 1 < kTokSteps / kTokAhead)
+      if (g + 1 < TS / kTokAhead)
         buf[k] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff(t + kTokAhead), 0, kStream));
       // bias, then the taps oldest first (the channel-major kernels' order)
@@ -299,9 +302,12 @@ __global__ __launch_bounds__(256) void causal_conv1d_tok_kernel(TokArgs a) {
 }
 
 template <int W>
-ssd_status launch_tok(const TokArgs &a, hipStream_t s) {
+ssd_status launch_tok(const TokArgs &a, bool short_waves, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.cblk * a.sblk));
-  hipLaunchKernelGGL((causal_conv1d_tok_kernel<W>), grid, dim3(256), 0, s, a);
+  if (short_waves)
+    hipLaunchKernelGGL((causal_conv1d_tok_kernel<W, kTokAhead>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((causal_conv1d_tok_kernel<W, kTokSteps>), grid, dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_LAUNCH;
 }
 
@@ -403,10 +409,16 @@ extern "C" ssd_status ssd_causal_conv1d_tokmajor(const float *x, int64_t x_strid
   a.S = seqlen;
   a.xs = x_stride;
   a.act = activation;
+  // 16-step waves when 32-step ones would leave fewer than two workgroups
+  // per CU (256 CUs), unless the state is updated in place over more than
+  // 16 steps (one wave must then cover every step)
+  const bool in_place = final_state && final_state == x_prev;
+  const bool short_waves = batch * cblk * sblk < 2 * 256 && !(in_place && seqlen > kTokAhead);
+  const int64_t ts = short_waves ? kTokAhead : kTokSteps;
   a.cblk = (uint32_t)cblk;
-  a.sblk = (uint32_t)sblk;
+  a.sblk = (uint32_t)((seqlen + 4 * ts - 1) / (4 * ts));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (width == 2) return launch_tok<2>(a, s);
-  if (width == 3) return launch_tok<3>(a, s);
-  return launch_tok<4>(a, s);
+  if (width == 2) return launch_tok<2>(a, short_waves, s);
+  if (width == 3) return launch_tok<3>(a, short_waves, s);
+  return launch_tok<4>(a, short_waves, s);
 }
