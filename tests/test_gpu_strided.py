@@ -171,11 +171,16 @@ def test_tokmajor_conv_matches_oracle(gpu_lib, shape, opts):
     np.testing.assert_array_equal(fin.cpu().numpy(), ref_fin.astype(np.float32))
 
 
-def test_tokmajor_conv_equals_the_channel_major_conv(gpu_lib):
+# [2, 264, 777] takes 16-step waves (a grid under two workgroups per CU),
+# [4, 1024, 4100] 32-step ones (528 workgroups), with a ragged last block
+@pytest.mark.parametrize("shape", [(2, 264, 777, 4), (4, 1024, 4100, 4)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_tokmajor_conv_equals_the_channel_major_conv(gpu_lib, shape):
     """Both layouts compute each output with the same taps in the same order:
     the results agree bit for bit."""
-    B, D, S, W = 2, 264, 777, 4
-    d = conv_inputs(B, D, S, W, seed=77, has_state=True)
+    B, D, S, W = shape
+    _say(f"  token-major vs channel-major conv1d B={B} D={D} S={S} W={W}")
+    d = conv_inputs(B, D, S, W, seed=77 + S, has_state=True)
     g = {k: v.cuda() for k, v in d.items()}
     ref, ref_fin = gpu_lib.causal_conv1d(g["x"], g["w"], g["bias"], g["conv_state"],
                                          return_final_state=True)
