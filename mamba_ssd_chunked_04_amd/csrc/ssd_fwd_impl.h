@@ -287,9 +287,10 @@ __device__ __forceinline__ int64_t umod32(int64_t a, int64_t b) {
 // folds an even number of groups itself, a dense call's late group ng-1-i is
 // dealt with its early partner i on one XCD, late members first, so each XCD
 // holds the same mix of long and short prologues and a CU's two workgroups
-// tend to be such a pair (headline main pass 39.4 -> 38.3 us).  (Its
-// divisions stay 64-bit: with udiv32 here the compiler spilled scalar
-// registers inside the block loop of the 256-token gated kernel, 1% slower.)
+// tend to be such a pair (headline main pass 39.4 -> 38.3 us).  (The
+// packed and the plain dense decode keep 64-bit divisions: with udiv32 there
+// the compiler spilled scalar registers inside the block loop of the
+// 256-token gated kernel, 1% slower.)
 __device__ __forceinline__ bool decode_tile(const Params &p, int64_t ngroups_here, int64_t &b,
                                             int64_t &h, int64_t &j, bool late_first = false) {
   const int64_t total = p.batch * p.H * ngroups_here;
