@@ -146,6 +146,23 @@ def test_no_final_state_and_bf16_out(gpu_lib):
     assert_close(out, ref_out, TOL["f16"] + 2 ** -8, "out (bf16 storage)")
 
 
+@pytest.mark.parametrize("cpw", [1, 2])
+def test_final_state_request_does_not_change_out(gpu_lib, cpw):
+    """Without the final state the main pass skips the state work after each
+    chunk group's last chunk; out is the same, bit for bit, as with the final
+    state, and both match the oracle (8 groups of one chunk or 4 of two, the
+    last one ragged)."""
+    _say(f"[case] final state on and off, chunks_per_wg={cpw}")
+    d = random_inputs(2, 900, 4, 64, 128, 2, seed=404, has_D=True, has_z=True)
+    ref_out, ref_fin = oracle_run(d)
+    out_f, fin = gpu_run(gpu_lib, d, 128, chunks_per_wg=cpw)
+    out_n, none = gpu_run(gpu_lib, d, 128, chunks_per_wg=cpw, ret_final=False)
+    assert none is None
+    assert np.array_equal(out_f, out_n)
+    assert_close(out_n, ref_out, TOL["f16"], f"out (chunks_per_wg={cpw})")
+    assert_close(fin, ref_fin, TOL["f16"], f"final_state (chunks_per_wg={cpw})")
+
+
 def test_determinism(gpu_lib):
     d = random_inputs(2, 700, 8, 64, 128, 2, seed=402, has_D=True, has_z=True, has_h0=True)
     a_out, a_fin = gpu_run(gpu_lib, d, 256, chunks_per_wg=1)
